@@ -1,0 +1,24 @@
+"""CPU oracle for exact attention (fp64, numpy).
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+benchmark's CPU-baseline leg may import this package.  The GPU library and its
+Python binding never import, call or link anything here, and nothing here
+imports them.
+
+Parity status of each function (the pins live in tests/test_oracle.py):
+
+* ``attention``         -- pinned (brute force, library cross-check, closed forms,
+                           invariants).
+* ``attention_online``  -- pinned (equals ``attention`` and the brute force for
+                           several tile widths, both recurrence forms).
+* ``split_bounds``, ``splitkv_partials``, ``combine`` -- pinned (combine of the
+                           partials equals unsplit attention; one split is the
+                           identity; empty chunks get weight zero).
+"""
+from .attention import (  # noqa: F401
+    attention,
+    attention_online,
+    combine,
+    split_bounds,
+    splitkv_partials,
+)
