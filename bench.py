@@ -1,0 +1,267 @@
+"""Benchmark of the attention forward hot path on one MI355X.
+
+Default run (N=1): the pages' benchmark shape (B=1, H=8, Nq=4096, Nk=8192,
+d=128, bf16, non-causal) through fa_fwd, W warm-up steps then exactly K timed
+steps; one JSON line on stdout. The line also carries the split-KV decode
+workload (B=64, Hq=32, Hkv=8, Nk=8192, 16 splits) timed the same way, the
+roofline of the dominant kernel, and the CPU oracle timed on a bounded sample.
+
+  python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--all]
+  python bench.py --only prefill|decode --steps 3   (short runs under a profiler)
+  python bench.py --copy-calib                       (plain copy of known size, for counter scaling)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import synth  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+PREFILL = "pages_shape_h8_q4096_kv8192"
+DECODE = "gqa_decode_b64_hq32_hkv8_kv8192"
+OTHER_PREFILL = ["batched_prefill_b4h16_n2048", "batched_prefill_b4h16_n2048_causal", "long_causal_h32_n16384"]
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "exact_io_aware_17_amd", "csrc")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_sha(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+FWD_SOURCES = ["fa_fwd.hip", "fa_common.h"]
+DEC_SOURCES = ["fa_splitkv.hip", "fa_common.h"]
+
+
+def traffic_from_profile(name, sources):
+    """HBM bytes per launch from a committed counter summary, or None when the
+    summary is missing or was taken from other kernel sources."""
+    path = os.path.join(PROFILES, name)
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"source_sha:\s*([0-9a-f]+)", text)
+    b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m or not b or m.group(1) != kernel_source_sha(sources):
+        return None
+    return float(b.group(1))
+
+
+def device_inputs(w, device):
+    import torch
+
+    def get(t, shape):
+        bits = synth.draw_bf16(w.seed, t, shape)
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(device)
+    return get(synth.TENSOR_Q, w.q_shape), get(synth.TENSOR_K, w.kv_shape), get(synth.TENSOR_V, w.kv_shape)
+
+
+def time_steps(step, steps, warmup):
+    """W untimed steps, then exactly K timed steps. Returns (wall seconds,
+    mean per-launch event milliseconds). Events are recorded on the stream the
+    kernels run on (the current torch stream, which the binding passes down)."""
+    import torch
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        evs[i][0].record()
+        step()
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    return wall, ev_ms
+
+
+def bench_prefill(w, steps, warmup, device):
+    import torch
+    import exact_io_aware_17_amd as fa
+    q, k, v = device_inputs(w, device)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=device)
+
+    def step():
+        fa.fa_fwd(q, k, v, o, lse, scale=w.scale, causal=w.causal)
+    wall, ev_ms = time_steps(step, steps, warmup)
+    return {"wall_s": wall, "ms_per_step": wall * 1e3 / steps, "kernel_ms": ev_ms,
+            "tflops": w.flops() / (wall / steps) / 1e12, "kernel_tflops": w.flops() / (ev_ms * 1e-3) / 1e12}
+
+
+def bench_decode(w, steps, warmup, device):
+    """Each step reads a different copy of K/V (three copies rotate) so that no
+    step finds its 2 GiB of K/V in the 256 MB last-level cache."""
+    import torch
+    import exact_io_aware_17_amd as fa
+    q, k, v = device_inputs(w, device)
+    copies = [(k, v)] + [(k.clone(), v.clone()) for _ in range(2)]
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=device)
+    ws = fa.workspace_for(q, w.num_splits)
+    it = [0]
+
+    def step():
+        kk, vv = copies[it[0] % len(copies)]
+        it[0] += 1
+        fa.fa_fwd_splitkv(q, kk, vv, o, lse, w.num_splits, ws, scale=w.scale)
+    wall, ev_ms = time_steps(step, steps, warmup)
+    nbytes = w.algorithmic_bytes()
+    return {"wall_s": wall, "ms_per_step": wall * 1e3 / steps, "kernel_ms": ev_ms,
+            "gbs": nbytes / (wall / steps) / 1e9, "kernel_gbs": nbytes / (ev_ms * 1e-3) / 1e9}
+
+
+def cpu_baseline(w, budget_s=15.0):
+    """The fp64 oracle on the host, head by head, until the budget is spent."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    group = w.Hq // w.Hkv
+    done = 0
+    t_total = 0.0
+    for b in range(w.B):
+        for h in range(w.Hq):
+            q, k, v = synth.inputs_f64(w, q_heads=[(b, h)], kv_heads=[(b, h // group)])
+            t0 = time.perf_counter()
+            oracle.attention(q[:, None], k[:, None], v[:, None], w.scale, w.causal)
+            t_total += time.perf_counter() - t0
+            done += 1
+            if t_total >= budget_s:
+                break
+        if t_total >= budget_s:
+            break
+    flops = w.flops() * done / (w.B * w.Hq)
+    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} of {w.B * w.Hq} (batch, head) slabs of {w.name}, all {w.Nq} query rows, "
+                      f"{t_total:.1f} s of fp64 numpy on the host"}
+
+
+def copy_calib(device, nbytes=1 << 30, steps=3):
+    """A plain device copy of known size, for scaling FETCH_SIZE / WRITE_SIZE."""
+    import torch
+    a = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    b = torch.empty_like(a)
+    a.fill_(1)
+    for _ in range(steps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calib_bytes": nbytes, "steps": steps}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--all", action="store_true", help="also time the other prefill workloads")
+    ap.add_argument("--only", choices=["prefill", "decode"], default=None)
+    ap.add_argument("--copy-calib", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    device = torch.device("cuda:0")
+    if args.copy_calib:
+        copy_calib(device)
+        return
+    from __graft_entry__ import _ensure_built
+    _ensure_built()
+
+    wp = synth.WORKLOADS[PREFILL]
+    wd = synth.WORKLOADS[DECODE]
+    if args.only == "prefill":
+        r = bench_prefill(wp, args.steps, args.warmup, device)
+        print(json.dumps({"only": "prefill", **r}))
+        return
+    if args.only == "decode":
+        r = bench_decode(wd, args.steps, args.warmup, device)
+        print(json.dumps({"only": "decode", **r}))
+        return
+
+    log(f"prefill {wp.name}: warmup {args.warmup}, steps {args.steps}")
+    rp = bench_prefill(wp, args.steps, args.warmup, device)
+    log(f"  {rp}")
+    log(f"decode {wd.name}: warmup {args.warmup}, steps {args.steps}")
+    rd = bench_decode(wd, args.steps, args.warmup, device)
+    log(f"  {rd}")
+    others = {}
+    if args.all:
+        for name in OTHER_PREFILL:
+            w = synth.WORKLOADS[name]
+            log(f"prefill {name}")
+            r = bench_prefill(w, args.steps, args.warmup, device)
+            others[name] = {"tflops": round(r["tflops"], 2), "kernel_tflops": round(r["kernel_tflops"], 2),
+                            "kernel_ms": round(r["kernel_ms"], 4),
+                            "pct_peak": round(100 * r["kernel_tflops"] / PEAK_BF16_TFLOPS, 2)}
+            log(f"  {others[name]}")
+
+    fwd_traffic = traffic_from_profile("fwd_bf16_pages_shape_traffic.md", FWD_SOURCES)
+    dec_traffic = traffic_from_profile("splitkv_decode_traffic.md", DEC_SOURCES)
+    line = {
+        "metric": "attention fwd TFLOPS (4*B*H*Nq*Nk*d per forward) on the pages' shape; decode HBM GB/s",
+        "value": round(rp["tflops"], 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(rp["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wp.name, "B": wp.B, "H": wp.Hq, "Nq": wp.Nq, "Nk": wp.Nk, "d": wp.d,
+                   "causal": wp.causal, "pct_of_bf16_peak": round(100 * rp["tflops"] / PEAK_BF16_TFLOPS, 2)},
+        "roofline": {"bound": "mfma", "achieved": round(rp["kernel_tflops"], 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(rp["kernel_tflops"] / PEAK_BF16_TFLOPS, 4),
+                     "traffic": fwd_traffic, "kernel_ms": round(rp["kernel_ms"], 5),
+                     "kernel": "fwd_bf16_kernel<128>"},
+        "decode": {"workload": wd.name, "metric": "decode HBM GB/s (algorithmic bytes / step time)",
+                   "value": round(rd["gbs"], 1), "unit": "GB/s", "ms_per_step": round(rd["ms_per_step"], 5),
+                   "roofline": {"bound": "hbm", "achieved": round(rd["kernel_gbs"], 1), "peak": PEAK_HBM_GBS,
+                                "unit": "GB/s", "frac": round(rd["kernel_gbs"] / PEAK_HBM_GBS, 4),
+                                "traffic": dec_traffic, "kernel_ms": round(rd["kernel_ms"], 5),
+                                "kernel": "splitkv_partial_kernel<128> + combine_kernel<128>"}},
+    }
+    if others:
+        line["other_prefill"] = others
+    if not args.no_cpu:
+        log("cpu baseline (oracle) ...")
+        line["cpu_baseline"] = cpu_baseline(wp)
+        log(f"  {line['cpu_baseline']}")
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,211 @@
+"""MI355X (gfx950) exact attention forward: Python binding of libfa.so.
+
+The binding only marshals arguments: every step of the computation runs in the
+library's HIP kernels. torch supplies device memory and streams. If the library
+is not built, loading it raises; there is no fallback path.
+
+Entry points with the C names (tensors in, status checked, nothing returned):
+    fa_fwd, fa_fwd_fp32, fa_fwd_splitkv, fa_combine, fa_splitkv_workspace_bytes,
+    fa_status_str
+Convenience wrappers that allocate the outputs:
+    forward(q, k, v, causal=False, scale=None)            -> (o, lse)
+    forward_fp32(q, k, v, causal=False, scale=None)       -> (o, lse)
+    decode(q, k, v, num_splits, causal=False, scale=None, workspace=None) -> (o, lse)
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libfa.so")
+
+FA_OK = 0
+STATUS_NAMES = {0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_UNSUPPORTED", 4: "FA_ERR_ALIGN",
+                5: "FA_ERR_WORKSPACE", 6: "FA_ERR_LAUNCH", 7: "FA_ERR_ARG"}
+
+# Exported symbols and their C signatures (mirrors include/fa.h).
+_P, _I, _F, _S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+SIGNATURES = {
+    "fa_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "fa_fwd_fp32": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "fa_splitkv_workspace_bytes": (_S, [_I, _I, _I, _I, _I]),
+    "fa_fwd_splitkv": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _P, _S, _P]),
+    "fa_combine": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
+    "fa_status_str": (ctypes.c_char_p, [_I]),
+}
+
+_lib = None
+
+
+class FaError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__(f"{fn} failed: {fa_status_str(status)}")
+
+
+def lib():
+    """Load libfa.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m exact_io_aware_17_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def fa_status_str(status: int) -> str:
+    return lib().fa_status_str(int(status)).decode()
+
+
+def _check(fn, status):
+    if status != FA_OK:
+        raise FaError(fn, status)
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None and t.numel() else ctypes.c_void_p(0)
+
+
+def _dims(q, k, v, dtype):
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype != dtype:
+            raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be [B, H, N, d]")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be on the GPU")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k, v must be on one device")
+    B, Hq, Nq, d = q.shape
+    Bk, Hkv, Nk, dk = k.shape
+    if v.shape != k.shape or Bk != B or dk != d:
+        raise ValueError("q/k/v shapes disagree")
+    del torch
+    return B, Hq, Hkv, Nq, Nk, d
+
+
+def _default_scale(d, scale):
+    return float(1.0 / math.sqrt(d)) if scale is None else float(scale)
+
+
+def _out_check(o, lse, q, odtype):
+    import torch
+    if o.dtype != odtype or tuple(o.shape) != tuple(q.shape) or not o.is_contiguous():
+        raise ValueError("o must be a contiguous tensor shaped like q")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != tuple(q.shape[:3]) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, Hq, Nq] tensor")
+
+
+def fa_fwd(q, k, v, o, lse, scale=None, causal=False, stream=None):
+    """bf16 forward into caller-provided o (bf16, like q) and lse (fp32 [B,Hq,Nq])."""
+    import torch
+    B, Hq, Hkv, Nq, Nk, d = _dims(q, k, v, torch.bfloat16)
+    _out_check(o, lse, q, torch.bfloat16)
+    st = lib().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Nq, Nk, d,
+                      _default_scale(d, scale), int(bool(causal)), _stream(stream))
+    _check("fa_fwd", st)
+
+
+def fa_fwd_fp32(q, k, v, o, lse, scale=None, causal=False, stream=None):
+    import torch
+    B, Hq, Hkv, Nq, Nk, d = _dims(q, k, v, torch.float32)
+    _out_check(o, lse, q, torch.float32)
+    st = lib().fa_fwd_fp32(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Nq, Nk, d,
+                           _default_scale(d, scale), int(bool(causal)), _stream(stream))
+    _check("fa_fwd_fp32", st)
+
+
+def fa_splitkv_workspace_bytes(B, Hq, Nq, d, num_splits) -> int:
+    return int(lib().fa_splitkv_workspace_bytes(B, Hq, Nq, d, num_splits))
+
+
+def fa_fwd_splitkv(q, k, v, o, lse, num_splits, workspace, scale=None, causal=False, stream=None):
+    """Split-KV forward; `workspace` is a device tensor of at least
+    fa_splitkv_workspace_bytes(...) bytes."""
+    import torch
+    B, Hq, Hkv, Nq, Nk, d = _dims(q, k, v, torch.bfloat16)
+    _out_check(o, lse, q, torch.bfloat16)
+    nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib().fa_fwd_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Nq, Nk, d,
+                              _default_scale(d, scale), int(bool(causal)), int(num_splits), _ptr(workspace),
+                              nbytes, _stream(stream))
+    _check("fa_fwd_splitkv", st)
+
+
+def fa_combine(o_part, lse_part, o, lse, stream=None):
+    """Merge o_part [B,Hq,S,Nq,d] fp32 / lse_part [B,Hq,S,Nq] fp32 into o (bf16) and lse."""
+    import torch
+    if o_part.dtype != torch.float32 or lse_part.dtype != torch.float32:
+        raise TypeError("partials must be float32")
+    if o_part.dim() != 5 or not o_part.is_contiguous() or not lse_part.is_contiguous():
+        raise ValueError("o_part must be a contiguous [B, Hq, S, Nq, d] tensor")
+    B, Hq, S, Nq, d = o_part.shape
+    if tuple(lse_part.shape) != (B, Hq, S, Nq):
+        raise ValueError("lse_part must be [B, Hq, S, Nq]")
+    if o.dtype != torch.bfloat16 or tuple(o.shape) != (B, Hq, Nq, d) or tuple(lse.shape) != (B, Hq, Nq):
+        raise ValueError("o must be bf16 [B, Hq, Nq, d] and lse [B, Hq, Nq]")
+    st = lib().fa_combine(_ptr(o_part), _ptr(lse_part), _ptr(o), _ptr(lse), B, Hq, Nq, d, S, _stream(stream))
+    _check("fa_combine", st)
+
+
+def forward(q, k, v, causal=False, scale=None, stream=None):
+    import torch
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    fa_fwd(q, k, v, o, lse, scale=scale, causal=causal, stream=stream)
+    return o, lse
+
+
+def forward_fp32(q, k, v, causal=False, scale=None, stream=None):
+    import torch
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    fa_fwd_fp32(q, k, v, o, lse, scale=scale, causal=causal, stream=stream)
+    return o, lse
+
+
+def workspace_for(q, num_splits):
+    """A device byte tensor large enough for fa_fwd_splitkv (256-byte aligned by torch's allocator)."""
+    import torch
+    B, Hq, Nq, d = q.shape
+    n = fa_splitkv_workspace_bytes(B, Hq, Nq, d, num_splits)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+
+
+def split_views(workspace, B, Hq, Nq, d, num_splits):
+    """(o_part, lse_part) views of a split-KV workspace (the layout fa.h documents)."""
+    import torch
+    rows = B * Hq * num_splits * Nq
+    ob = (rows * d * 4 + 255) // 256 * 256
+    o_part = workspace[: rows * d * 4].view(torch.float32).view(B, Hq, num_splits, Nq, d)
+    lse_part = workspace[ob: ob + rows * 4].view(torch.float32).view(B, Hq, num_splits, Nq)
+    return o_part, lse_part
+
+
+def decode(q, k, v, num_splits, causal=False, scale=None, workspace=None, stream=None):
+    import torch
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = workspace_for(q, num_splits)
+    fa_fwd_splitkv(q, k, v, o, lse, num_splits, workspace, scale=scale, causal=causal, stream=stream)
+    return o, lse

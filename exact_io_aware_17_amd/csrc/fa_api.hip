@@ -1,0 +1,149 @@
+// C ABI of the attention library: host-side argument checks, workspace sizing
+// and dispatch to the kernel launchers. No device memory is allocated here and
+// nothing is enqueued unless every check passes.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/fa.h"
+#include "fa_internal.h"
+
+namespace {
+
+constexpr int kMaxSplits = 1024;
+constexpr long kMaxGridX = 2147483647L;
+constexpr long kMaxGridYZ = 65535L;
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Element count of a [a, b, c, d] tensor, or -1 if it does not fit in int64
+// with room to spare for byte offsets.
+long long elems4(long long a, long long b, long long c, long long d) {
+  const long long lim = (1LL << 60);
+  long long r = 1;
+  for (long long x : {a, b, c, d}) {
+    if (x < 0) return -1;
+    if (x != 0 && r > lim / x) return -1;
+    r *= x;
+  }
+  return r;
+}
+
+fa_status check_common(const void* q, const void* k, const void* v, const void* o, const void* lse, int B,
+                       int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal) {
+  if (B < 0 || Nq < 0 || Nk < 0 || Hq < 1 || Hkv < 1 || d < 1) return FA_ERR_SHAPE;
+  if (Hq % Hkv != 0) return FA_ERR_SHAPE;
+  const long long nq = elems4(B, Hq, Nq, d), nkv = elems4(B, Hkv, Nk, d);
+  if (nq < 0 || nkv < 0) return FA_ERR_SHAPE;
+  if ((long long)B * Hq > 0x7fffffffLL || (long long)B * Hkv > 0x7fffffffLL) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_ARG;
+  if (causal != 0 && causal != 1) return FA_ERR_ARG;
+  // Pointers of empty tensors may be NULL (allocators hand out NULL for them).
+  if (nq > 0 && (!q || !o || !lse)) return FA_ERR_NULL;
+  if (nkv > 0 && (!k || !v)) return FA_ERR_NULL;
+  for (const void* p : {q, k, v, o, lse})
+    if (p && !aligned16(p)) return FA_ERR_ALIGN;
+  return FA_OK;
+}
+
+fa_status launched(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH; }
+
+size_t round256(size_t x) { return (x + 255u) & ~(size_t)255u; }
+
+// Workspace layout of the split path: O_s then (256-aligned) LSE_s.
+bool split_ws_sizes(int B, int Hq, int Nq, int d, int S, size_t* o_bytes, size_t* total) {
+  if (B < 0 || Hq < 1 || Nq < 0 || S < 1 || S > kMaxSplits || (d != 64 && d != 128)) return false;
+  const long long rows = elems4(B, Hq, S, Nq);
+  if (rows < 0 || rows > (1LL << 50)) return false;
+  *o_bytes = round256((size_t)rows * (size_t)d * 4u);
+  *total = *o_bytes + round256((size_t)rows * 4u);
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fa_status_str(fa_status s) {
+  switch (s) {
+    case FA_OK: return "FA_OK";
+    case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
+    case FA_ERR_SHAPE: return "FA_ERR_SHAPE: invalid or overflowing sizes, or Hq % Hkv != 0";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: head size or mode not implemented";
+    case FA_ERR_ALIGN: return "FA_ERR_ALIGN: a pointer is not 16-byte aligned (workspace: 256-byte)";
+    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing or too small";
+    case FA_ERR_LAUNCH: return "FA_ERR_LAUNCH: kernel launch failed";
+    case FA_ERR_ARG: return "FA_ERR_ARG: scale not finite and > 0, causal not 0/1, or bad split count";
+  }
+  return "unknown fa_status";
+}
+
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
+                 int Nq, int Nk, int d, float scale, int causal, void* stream) {
+  fa_status st = check_common(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal);
+  if (st != FA_OK) return st;
+  if (fa::fwd_bf16_grid(B, Hq, Nq) > kMaxGridX) return FA_ERR_UNSUPPORTED;
+  fa::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal, stream};
+  return launched(fa::launch_fwd_bf16(a));
+}
+
+fa_status fa_fwd_fp32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int Hq,
+                      int Hkv, int Nq, int Nk, int d, float scale, int causal, void* stream) {
+  fa_status st = check_common(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal);
+  if (st != FA_OK) return st;
+  if (fa::fwd_fp32_grid(B, Hq, Nq) > kMaxGridX) return FA_ERR_UNSUPPORTED;
+  fa::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal, stream};
+  return launched(fa::launch_fwd_fp32(a));
+}
+
+size_t fa_splitkv_workspace_bytes(int B, int Hq, int Nq, int d, int num_splits) {
+  size_t ob = 0, total = 0;
+  if (!split_ws_sizes(B, Hq, Nq, d, num_splits, &ob, &total)) return 0;
+  return total;
+}
+
+fa_status fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+                         int Hkv, int Nq, int Nk, int d, float scale, int causal, int num_splits,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  fa_status st = check_common(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal);
+  if (st != FA_OK) return st;
+  if (num_splits < 1 || num_splits > kMaxSplits) return FA_ERR_ARG;
+  size_t ob = 0, total = 0;
+  if (!split_ws_sizes(B, Hq, Nq, d, num_splits, &ob, &total)) return FA_ERR_SHAPE;
+  const long long rows = (long long)B * Hq * Nq;
+  if (rows > 0) {
+    if (!workspace || workspace_bytes < total) return FA_ERR_WORKSPACE;
+    if (((uintptr_t)workspace & 255u) != 0) return FA_ERR_ALIGN;
+  }
+  if (fa::splitkv_grid(B, Hq, Hkv, Nq, num_splits) > kMaxGridX || B > kMaxGridYZ || Hkv > kMaxGridYZ)
+    return FA_ERR_UNSUPPORTED;
+  if (fa::combine_grid(B, Hq, Nq) > kMaxGridX) return FA_ERR_UNSUPPORTED;
+  if (rows == 0) return FA_OK;
+  float* o_part = (float*)workspace;
+  float* lse_part = (float*)((char*)workspace + ob);
+  fa::FwdArgs f{q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal, stream};
+  fa::SplitArgs sa{f, num_splits, o_part, lse_part};
+  st = launched(fa::launch_splitkv_partial(sa));
+  if (st != FA_OK) return st;
+  fa::CombineArgs ca{o_part, lse_part, o, lse, B, Hq, Nq, d, num_splits, stream};
+  return launched(fa::launch_combine(ca));
+}
+
+fa_status fa_combine(const float* o_part, const float* lse_part, void* o, float* lse, int B, int Hq, int Nq,
+                     int d, int num_splits, void* stream) {
+  if (B < 0 || Hq < 1 || Nq < 0) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (num_splits < 1 || num_splits > kMaxSplits) return FA_ERR_ARG;
+  size_t ob = 0, total = 0;
+  if (!split_ws_sizes(B, Hq, Nq, d, num_splits, &ob, &total)) return FA_ERR_SHAPE;
+  const long long rows = (long long)B * Hq * Nq;
+  if (rows == 0) return FA_OK;
+  if (!o_part || !lse_part || !o || !lse) return FA_ERR_NULL;
+  for (const void* p : {(const void*)o_part, (const void*)lse_part, (const void*)o, (const void*)lse})
+    if (!aligned16(p)) return FA_ERR_ALIGN;
+  if (fa::combine_grid(B, Hq, Nq) > kMaxGridX) return FA_ERR_UNSUPPORTED;
+  fa::CombineArgs ca{o_part, lse_part, o, lse, B, Hq, Nq, d, num_splits, stream};
+  return launched(fa::launch_combine(ca));
+}
+
+}  // extern "C"

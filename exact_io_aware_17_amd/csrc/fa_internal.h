@@ -1,0 +1,49 @@
+// Internal host-side interface between the C ABI layer and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace fa {
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int B, Hq, Hkv, Nq, Nk, d;
+  float scale;
+  int causal;
+  void* stream;
+};
+
+struct SplitArgs {
+  FwdArgs f;
+  int num_splits;
+  float* o_part;    // [B, Hq, S, Nq, d]
+  float* lse_part;  // [B, Hq, S, Nq]
+};
+
+struct CombineArgs {
+  const float* o_part;
+  const float* lse_part;
+  void* o;
+  float* lse;
+  int B, Hq, Nq, d, num_splits;
+  void* stream;
+};
+
+hipError_t launch_fwd_bf16(const FwdArgs& a);
+hipError_t launch_fwd_fp32(const FwdArgs& a);
+hipError_t launch_splitkv_partial(const SplitArgs& a);
+hipError_t launch_combine(const CombineArgs& a);
+
+// Grid sizes (workgroups) the launchers would use; the ABI layer checks them
+// against the hardware limit before launching.
+long fwd_bf16_grid(int B, int Hq, int Nq);
+long fwd_fp32_grid(int B, int Hq, int Nq);
+long splitkv_grid(int B, int Hq, int Hkv, int Nq, int num_splits);
+long combine_grid(int B, int Hq, int Nq);
+
+}  // namespace fa

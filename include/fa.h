@@ -1,0 +1,126 @@
+/*
+ * fa.h -- C ABI of the MI355X (gfx950) exact-attention forward library.
+ *
+ * What is computed.  For each batch b and query head h, with KV head
+ * g = h / (Hq / Hkv):
+ *     S = (Q[b,h] K[b,g]^T) * scale,   P = row-softmax(S),   O[b,h] = P V[b,g]
+ * and per query row LSE = ln(sum_j exp(S_ij)) over the visible keys.
+ * This is the standard self-attention of the "flash attention v3 paper"
+ * search-result page (standard self-attention snippet: S = QK^T, row softmax,
+ * O = PV), with the scale placed after the product as in the "Flash Attention
+ * 2 algorithm" pseudocode of "Flash Attention on the 5090 in CUDA C++".
+ * It is computed exactly, tile by tile, with the online softmax of that page's
+ * "v1 -- basic version" (running max, running denominator, rescaled O), so the
+ * Nq x Nk score matrix is never written to memory ("Flash Attention",
+ * aiunderstanding.org: deep dive).
+ *
+ * Readings where the pages say nothing (fixed here):
+ *   - layout: every tensor is contiguous row-major, d innermost:
+ *       q, o : [B, Hq, Nq, d]     k, v : [B, Hkv, Nk, d]     lse : [B, Hq, Nq]
+ *   - causal: key j is visible to query i iff j <= i + (Nk - Nq)
+ *     (lower-triangular when Nq == Nk; aligned to the last key otherwise);
+ *   - a query row with no visible key gets O = 0 and LSE = -inf;
+ *   - LSE is the natural log of the sum of exp of the *scaled* scores.
+ *
+ * Conventions shared by every entry point.
+ *   - All tensor pointers are device pointers owned by the caller.  The
+ *     library allocates nothing, frees nothing and keeps no global state.
+ *   - bf16 tensors are IEEE bfloat16 bit patterns (uint16); fp32 are float.
+ *   - Tensor pointers must be 16-byte aligned.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Work is enqueued asynchronously; the library never synchronizes.
+ *   - Arguments are checked on the host before anything is enqueued.  On any
+ *     error nothing is enqueued and a non-zero fa_status is returned.
+ *   - A failed kernel launch returns FA_ERR_LAUNCH.  The check reads (and so
+ *     clears) the calling thread's pending HIP error.
+ *   - B, Nq, Nk may be 0 (nothing to compute, or every row without keys).
+ *     Hq, Hkv >= 1 and Hq % Hkv == 0.  d must be 64 or 128.
+ *     scale must be finite and > 0.  causal must be 0 or 1.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fa_status {
+  FA_OK = 0,
+  FA_ERR_NULL = 1,        /* a required pointer is NULL */
+  FA_ERR_SHAPE = 2,       /* negative size, Hq % Hkv != 0, or sizes overflow */
+  FA_ERR_UNSUPPORTED = 3, /* head size or mode not implemented */
+  FA_ERR_ALIGN = 4,       /* a tensor pointer is not 16-byte aligned */
+  FA_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required */
+  FA_ERR_LAUNCH = 6,      /* the HIP runtime rejected a kernel launch */
+  FA_ERR_ARG = 7          /* scale not finite and > 0, causal not 0/1, bad split count */
+} fa_status;
+
+/*
+ * fa_fwd -- bf16 attention forward (prefill).
+ * q [B,Hq,Nq,d], k/v [B,Hkv,Nk,d] bf16 in; o [B,Hq,Nq,d] bf16 out (round to
+ * nearest even), lse [B,Hq,Nq] fp32 out.  Products run in bf16 with fp32
+ * accumulation; the softmax runs in fp32; probabilities are rounded to bf16
+ * before the P.V product while the row sums use the unrounded values.
+ * o and lse must not overlap the inputs.
+ */
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                 float scale, int causal, void* stream);
+
+/*
+ * fa_fwd_fp32 -- the same operation in fp32 throughout (debug / reference
+ * path; plain FMA arithmetic, no matrix cores).  Same layout and rules as
+ * fa_fwd with float tensors.
+ */
+fa_status fa_fwd_fp32(const float* q, const float* k, const float* v, float* o, float* lse,
+                      int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                      float scale, int causal, void* stream);
+
+/*
+ * fa_splitkv_workspace_bytes -- bytes of workspace fa_fwd_splitkv needs:
+ * partial outputs O_s [B,Hq,S,Nq,d] fp32 followed (at the next 256-byte
+ * boundary) by partial LSE_s [B,Hq,S,Nq] fp32.  Returns 0 for invalid sizes.
+ */
+size_t fa_splitkv_workspace_bytes(int B, int Hq, int Nq, int d, int num_splits);
+
+/*
+ * fa_fwd_splitkv -- split-KV forward (decode): the keys are cut into
+ * num_splits contiguous chunks, chunk s = [s*C, min(Nk, (s+1)*C)) with
+ * C = ceil(Nk / num_splits).  A first kernel writes, per chunk, the exact
+ * attention of every query row over that chunk alone (normalised O_s in fp32
+ * and LSE_s) into the workspace; a second kernel (the same as fa_combine)
+ * merges them with LSE weights into o (bf16) and lse (fp32).  A chunk with no
+ * key has LSE_s = -inf and weight 0.  Split partial results and their merge
+ * follow the online-softmax rescale of the "v1 -- basic version" bullets
+ * applied to whole chunks; partial-softmax merging is the step the
+ * FlashDecoding++ snippet of the "flash attention v3 paper" page names as costly.
+ * Requires 1 <= num_splits <= 1024, (Hq/Hkv)*Nq <= 256 query rows per KV head,
+ * and workspace_bytes >= fa_splitkv_workspace_bytes(B,Hq,Nq,d,num_splits).
+ * The workspace (device memory, caller-owned, 256-byte aligned) holds the
+ * partial results after the call and may be inspected by the caller.
+ */
+fa_status fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                         int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                         float scale, int causal, int num_splits,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fa_combine -- LSE-weighted merge of per-chunk results.
+ * o_part [B,Hq,S,Nq,d] fp32, lse_part [B,Hq,S,Nq] fp32 in; o [B,Hq,Nq,d] bf16
+ * and lse [B,Hq,Nq] fp32 out.  With M = max_s LSE_s, w_s = exp(LSE_s - M):
+ * O = sum_s w_s O_s / sum_s w_s, LSE = M + ln(sum_s w_s); rows whose chunks
+ * are all empty get O = 0, LSE = -inf.  1 <= num_splits <= 1024.
+ */
+fa_status fa_combine(const float* o_part, const float* lse_part, void* o, float* lse,
+                     int B, int Hq, int Nq, int d, int num_splits, void* stream);
+
+/* fa_status_str -- static, human-readable name of a status code. */
+const char* fa_status_str(fa_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

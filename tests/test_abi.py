@@ -1,0 +1,138 @@
+"""The C ABI on the host (no GPU): the library loads, exports every function
+include/fa.h declares with the parameter count the binding assumes, and rejects
+bad arguments with the documented status before touching the GPU."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import exact_io_aware_17_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+P = 0x10000  # a 16-byte-aligned host address: never dereferenced, every call below fails validation
+
+
+def _declarations():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    decls = {}
+    for m in re.finditer(r"^\s*(fa_status|size_t|const char\s*\*)\s*(fa_\w+)\s*\(([^)]*)\)\s*;", text, re.M | re.S):
+        params = [p.strip() for p in m.group(3).split(",") if p.strip()]
+        decls[m.group(2)] = (m.group(1), len(params))
+    return decls
+
+
+def test_header_declarations_found():
+    d = _declarations()
+    assert set(d) == {"fa_fwd", "fa_fwd_fp32", "fa_splitkv_workspace_bytes", "fa_fwd_splitkv", "fa_combine",
+                      "fa_status_str"}
+
+
+def test_library_exports_every_declared_symbol():
+    lib = fa.lib()
+    for name, (_, nparams) in _declarations().items():
+        assert hasattr(lib, name), name
+        assert name in fa.SIGNATURES, name
+        assert len(fa.SIGNATURES[name][1]) == nparams, name
+
+
+def test_status_strings():
+    for code, name in fa.STATUS_NAMES.items():
+        assert fa.fa_status_str(code).startswith(name)
+    assert "unknown" in fa.fa_status_str(99)
+
+
+def _fwd(entry="fa_fwd", q=P, k=P, v=P, o=P, lse=P, B=1, Hq=2, Hkv=1, Nq=16, Nk=16, d=128, scale=0.1, causal=0):
+    return getattr(fa.lib(), entry)(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal, None)
+
+
+@pytest.mark.parametrize("entry", ["fa_fwd", "fa_fwd_fp32"])
+def test_forward_argument_checks(entry):
+    f = lambda **kw: _fwd(entry, **kw)  # noqa: E731
+    for name in ("q", "k", "v", "o", "lse"):
+        assert f(**{name: None}) == 1, name
+        assert f(**{name: P + 2}) == 4, name
+        assert f(**{name: P + 8}) == 4, name
+    assert f(Hq=3, Hkv=2) == 2
+    assert f(Hkv=0) == 2
+    assert f(B=-1) == 2
+    assert f(Nq=-5) == 2
+    assert f(Nk=-1) == 2
+    assert f(B=1 << 30, Hq=1 << 20, Hkv=1 << 20) == 2
+    assert f(d=96) == 3
+    assert f(d=256) == 3
+    for s in (0.0, -0.5, math.inf, math.nan):
+        assert f(scale=s) == 7, s
+    assert f(causal=2) == 7
+    assert f(causal=-1) == 7
+
+
+def test_empty_tensors_may_be_null_but_shapes_still_checked():
+    # An empty K/V (Nk == 0) with NULL k, v is valid, so only check the cases
+    # that still fail before any launch.
+    assert _fwd(k=None, v=None, Nk=0, d=96) == 3
+    assert _fwd(q=None, o=None, lse=None, Nq=0, Hq=3, Hkv=2) == 2
+
+
+def test_workspace_bytes():
+    ws = fa.fa_splitkv_workspace_bytes
+    rows = 64 * 32 * 16 * 1
+    o_bytes = (rows * 128 * 4 + 255) // 256 * 256
+    assert ws(64, 32, 1, 128, 16) == o_bytes + (rows * 4 + 255) // 256 * 256
+    assert ws(1, 1, 1, 64, 1) == 256 + 256
+    assert ws(0, 4, 1, 128, 4) == 0 + 0
+    assert ws(1, 1, 1, 96, 4) == 0
+    assert ws(1, 1, 1, 128, 0) == 0
+    assert ws(1, 1, 1, 128, 1025) == 0
+    assert ws(-1, 1, 1, 128, 2) == 0
+
+
+def _split(q=P, k=P, v=P, o=P, lse=P, B=2, Hq=8, Hkv=2, Nq=1, Nk=100, d=128, scale=0.1, causal=0, S=4,
+           ws=0x100000, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = fa.fa_splitkv_workspace_bytes(B, Hq, Nq, d, S)
+    return fa.lib().fa_fwd_splitkv(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal, S, ws, ws_bytes, None)
+
+
+def test_splitkv_argument_checks():
+    assert _split(S=0) == 7
+    assert _split(S=1025) == 7
+    assert _split(ws=None) == 5
+    assert _split(ws_bytes=100) == 5
+    assert _split(ws=0x100000 + 16) == 4
+    assert _split(q=None) == 1
+    assert _split(Hq=7) == 2
+    assert _split(d=80) == 3
+    assert _split(scale=-1.0) == 7
+    assert _split(B=70000) == 3  # grid z limit
+
+
+def test_combine_argument_checks():
+    c = fa.lib().fa_combine
+    assert c(P, P, P, P, 2, 4, 1, 128, 0, None) == 7
+    assert c(None, P, P, P, 2, 4, 1, 128, 4, None) == 1
+    assert c(P, P, P + 4, P, 2, 4, 1, 128, 4, None) == 4
+    assert c(P, P, P, P, 2, 4, 1, 32, 4, None) == 3
+    assert c(P, P, P, P, -2, 4, 1, 128, 4, None) == 2
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(fa, "_lib", None)
+    monkeypatch.setattr(fa, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        fa.lib()
+
+
+def test_product_path_does_not_import_oracle():
+    """The package and its sources never reference the test oracle."""
+    pkg = os.path.join(ROOT, "exact_io_aware_17_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for fn in files:
+            if fn.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, fn)).read()
+                assert "import oracle" not in text and "from oracle" not in text, fn
+                assert "oracle/" not in text, fn

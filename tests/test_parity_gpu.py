@@ -1,0 +1,287 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the
+same seeded inputs. Tolerances: max|O - O_ref| <= 2e-2 and max|LSE - LSE_ref|
+<= 1e-3 for bf16 inputs with fp32 accumulation; 1e-5 for the fp32 path."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_helpers import (F32_TOL, assert_close, device_inputs, errors, oracle_full, oracle_sample,
+                         sample_rows, say)
+
+pytestmark = pytest.mark.gpu
+
+W = synth.WORKLOADS
+
+
+def _fa():
+    import exact_io_aware_17_amd as fa
+    fa.lib()
+    return fa
+
+
+def _run_fwd(w, fp32=False):
+    import torch
+    fa = _fa()
+    q, k, v = device_inputs(w, bf16=not fp32)
+    say(f"  launch {'fa_fwd_fp32' if fp32 else 'fa_fwd'} {w}")
+    if fp32:
+        o, lse = fa.forward_fp32(q, k, v, causal=w.causal, scale=w.scale)
+    else:
+        o, lse = fa.forward(q, k, v, causal=w.causal, scale=w.scale)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+
+
+SMALL = [
+    W["single_head_n256_d64"],
+    synth.Workload("ragged_gqa", 2, 4, 2, 200, 333, 128),
+    synth.Workload("ragged_gqa_causal", 2, 4, 2, 200, 333, 128, causal=True),
+    synth.Workload("more_queries_than_keys_causal_d64", 1, 3, 1, 130, 70, 64, causal=True),
+    synth.Workload("one_query_one_key", 1, 1, 1, 1, 1, 128),
+    synth.Workload("keys_below_one_tile", 1, 2, 2, 300, 17, 128),
+    synth.Workload("square_causal_3_tiles", 1, 2, 2, 384, 384, 128, causal=True),
+    synth.Workload("causal_d64_ragged", 2, 2, 1, 257, 257, 64, causal=True, seed=3),
+]
+
+
+@pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name)
+def test_bf16_full_oracle(w):
+    say(f"case bf16 full {w.name}")
+    o, lse = _run_fwd(w)
+    o_ref, lse_ref = oracle_full(w)
+    assert_close(errors(o, o_ref, lse, lse_ref), what=w.name)
+
+
+@pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name)
+def test_fp32_full_oracle(w):
+    say(f"case fp32 full {w.name}")
+    o, lse = _run_fwd(w, fp32=True)
+    o_ref, lse_ref = oracle_full(w, bf16=False)
+    assert_close(errors(o, o_ref, lse, lse_ref), F32_TOL, F32_TOL, what=w.name + " fp32")
+
+
+LARGE = ["batched_prefill_b4h16_n2048", "batched_prefill_b4h16_n2048_causal", "pages_shape_h8_q4096_kv8192",
+         "long_causal_h32_n16384"]
+
+
+@pytest.mark.parametrize("name", LARGE)
+def test_bf16_full_size_sampled(name):
+    """Full-size launch (the configuration the benchmark times); the oracle
+    computes sampled rows of sampled heads one by one."""
+    w = W[name]
+    say(f"case bf16 full-size {name}")
+    o, lse = _run_fwd(w)
+    heads = sorted({(0, 0), (w.B - 1, w.Hq - 1), (w.B // 2, w.Hq // 2)})
+    rows = sample_rows(w.Nq, seed=hash(name) % 1000)
+    o_ref, lse_ref = oracle_sample(w, heads, rows)
+    got_o = np.stack([o[b, h][rows] for (b, h) in heads])
+    got_l = np.stack([lse[b, h][rows] for (b, h) in heads])
+    assert_close(errors(got_o, o_ref, got_l, lse_ref), what=name)
+    assert np.isfinite(lse).all() and np.isfinite(o).all()
+
+
+def test_fp32_batched_sampled():
+    w = W["batched_prefill_b4h16_n2048_causal"]
+    say("case fp32 full-size batched causal")
+    o, lse = _run_fwd(w, fp32=True)
+    heads = [(0, 0), (3, 15)]
+    rows = sample_rows(w.Nq, n_random=8)
+    o_ref, lse_ref = oracle_sample(w, heads, rows, bf16=False)
+    got_o = np.stack([o[b, h][rows] for (b, h) in heads])
+    got_l = np.stack([lse[b, h][rows] for (b, h) in heads])
+    assert_close(errors(got_o, o_ref, got_l, lse_ref), F32_TOL, F32_TOL, what="fp32 batched causal")
+
+
+def _run_decode(w, fetch_partials=False):
+    import torch
+    fa = _fa()
+    q, k, v = device_inputs(w)
+    ws = fa.workspace_for(q, w.num_splits)
+    say(f"  launch fa_fwd_splitkv {w}")
+    o, lse = fa.decode(q, k, v, w.num_splits, causal=w.causal, scale=w.scale, workspace=ws)
+    torch.cuda.synchronize()
+    out = (o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64))
+    if fetch_partials:
+        op, lp = fa.split_views(ws, w.B, w.Hq, w.Nq, w.d, w.num_splits)
+        out = out + (op.cpu().numpy().astype(np.float64), lp.cpu().numpy().astype(np.float64))
+    return out
+
+
+def test_decode_full_size():
+    """GQA split-KV decode at full size; oracle on every row of three batches,
+    for both the merged result and the per-chunk partials."""
+    w = W["gqa_decode_b64_hq32_hkv8_kv8192"]
+    say("case decode full-size")
+    o, lse, op, lp = _run_decode(w, fetch_partials=True)
+    group = w.Hq // w.Hkv
+    for b in (0, 37, 63):
+        q, k, v = synth.inputs_f64(w, q_heads=[(b, h) for h in range(w.Hq)],
+                                   kv_heads=[(b, g) for g in range(w.Hkv)])
+        q4 = q[None]
+        k4 = k[None]
+        v4 = v[None]
+        o_ref, l_ref = oracle.attention(q4, k4, v4, w.scale, False)
+        assert_close(errors(o[b], o_ref[0], lse[b], l_ref[0]), what=f"decode b={b}")
+        op_ref, lp_ref = oracle.splitkv_partials(q4, k4, v4, w.scale, w.num_splits)
+        e = errors(op[b], op_ref[0], lp[b], lp_ref[0])
+        assert_close(e, what=f"decode partials b={b}")
+        assert group == 4
+
+
+DECODE_EDGE = [
+    synth.Workload("nondividing_splits", 2, 8, 2, 1, 1000, 128, num_splits=7),
+    synth.Workload("one_split", 1, 4, 4, 1, 777, 128, num_splits=1),
+    synth.Workload("more_splits_than_keys", 1, 4, 1, 1, 5, 128, num_splits=9),
+    synth.Workload("multi_query_causal", 2, 6, 2, 3, 300, 128, causal=True, num_splits=4),
+    synth.Workload("decode_d64_gqa8", 3, 16, 2, 1, 2048, 64, num_splits=16),
+    synth.Workload("rows_over_32", 1, 40, 1, 2, 513, 128, num_splits=3),
+]
+
+
+@pytest.mark.parametrize("w", DECODE_EDGE, ids=lambda w: w.name)
+def test_decode_edge_cases(w):
+    say(f"case decode {w.name}")
+    o, lse, op, lp = _run_decode(w, fetch_partials=True)
+    q, k, v = synth.inputs_f64(w)
+    o_ref, l_ref = oracle.attention(q, k, v, w.scale, w.causal)
+    assert_close(errors(o, o_ref, lse, l_ref), what=w.name)
+    op_ref, lp_ref = oracle.splitkv_partials(q, k, v, w.scale, w.num_splits, w.causal)
+    assert_close(errors(op, op_ref, lp, lp_ref), what=w.name + " partials")
+
+
+def test_combine_entry_point():
+    """fa_combine alone, on seeded random partials (some chunks empty)."""
+    import torch
+    fa = _fa()
+    r = np.random.default_rng(5)
+    B, Hq, S, Nq, d = 2, 3, 5, 4, 128
+    op = r.standard_normal((B, Hq, S, Nq, d)).astype(np.float32)
+    lp = (r.standard_normal((B, Hq, S, Nq)) * 3).astype(np.float32)
+    lp[0, 0, 1] = -np.inf
+    lp[1, 2, :, 0] = -np.inf   # a row whose chunks are all empty
+    op[1, 2, :, 0] = 0.0
+    o = torch.empty((B, Hq, Nq, d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device="cuda")
+    say("case fa_combine")
+    fa.fa_combine(torch.from_numpy(op).cuda(), torch.from_numpy(lp).cuda(), o, lse)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.combine(op.astype(np.float64), lp.astype(np.float64))
+    assert_close(errors(o.float().cpu().numpy(), o_ref, lse.cpu().numpy(), l_ref), what="combine")
+    assert np.all(o[1, 2, 0].float().cpu().numpy() == 0)
+
+
+def _bf16_dev(x):
+    import torch
+    return torch.from_numpy(synth.bf16_bits(x.astype(np.float32)).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def test_structured_inputs():
+    """Closed forms on the GPU: identical keys give the column mean of V, a
+    one-hot query with a large logit selects one V row, V = 1 gives O = 1."""
+    import torch
+    fa = _fa()
+    r = np.random.default_rng(9)
+    Nq, Nk, d = 130, 300, 128
+    q = r.standard_normal((1, 2, Nq, d))
+    krow = r.standard_normal(d)
+    k = np.broadcast_to(krow, (1, 2, Nk, d)).copy()
+    v = r.standard_normal((1, 2, Nk, d))
+    qb, kb, vb = (_bf16_dev(x) for x in (q, k, v))
+    say("case structured identical keys")
+    o, lse = fa.forward(qb, kb, vb, scale=0.088388346)
+    torch.cuda.synchronize()
+    vv = vb.float().cpu().numpy().astype(np.float64)
+    o_exp = np.broadcast_to(vv.mean(axis=2, keepdims=True), o.shape)
+    assert np.max(np.abs(o.float().cpu().numpy() - o_exp)) <= 1e-2
+    qq = qb.float().cpu().numpy().astype(np.float64)
+    kk = kb.float().cpu().numpy().astype(np.float64)[0, 0, 0]
+    lse_exp = np.float64(np.float32(0.088388346)) * (qq @ kk) + np.log(Nk)
+    assert np.max(np.abs(lse.cpu().numpy() - lse_exp)) <= 1e-3
+    # One-hot selection: Q_i = e_{t(i)}, K_j = 64 e_j (Nk = d), scale 1 -> logit 64.
+    t = r.integers(0, d, size=Nq)
+    q1 = np.zeros((1, 1, Nq, d))
+    q1[0, 0, np.arange(Nq), t] = 1.0
+    k1 = (64.0 * np.eye(d))[None, None]
+    v1 = r.standard_normal((1, 1, d, d))
+    say("case structured one-hot")
+    o, lse = fa.forward(_bf16_dev(q1), _bf16_dev(k1), _bf16_dev(v1), scale=1.0)
+    torch.cuda.synchronize()
+    v1b = synth.bf16_bits_to_f32(synth.bf16_bits(v1.astype(np.float32))).astype(np.float64)
+    assert np.max(np.abs(o.float().cpu().numpy()[0, 0] - v1b[0, 0, t])) <= 1e-2
+    assert np.max(np.abs(lse.cpu().numpy()[0, 0] - 64.0)) <= 1e-3
+    say("case structured V = 1")
+    o, _ = fa.forward(qb, _bf16_dev(r.standard_normal((1, 2, Nk, d))), _bf16_dev(np.ones((1, 2, Nk, d))),
+                      causal=True)
+    torch.cuda.synchronize()
+    assert np.max(np.abs(o.float().cpu().numpy() - 1.0)) <= 8e-3
+
+
+def test_gqa_equals_repeated_kv():
+    import torch
+    fa = _fa()
+    w = synth.Workload("gqa", 2, 8, 2, 256, 320, 128, causal=True)
+    q, k, v = device_inputs(w)
+    say("case GQA vs repeated-KV MHA")
+    o1, l1 = fa.forward(q, k, v, causal=True)
+    o2, l2 = fa.forward(q, k.repeat_interleave(4, dim=1).contiguous(), v.repeat_interleave(4, dim=1).contiguous(),
+                        causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_deterministic():
+    import torch
+    fa = _fa()
+    w = W["batched_prefill_b4h16_n2048_causal"]
+    q, k, v = device_inputs(w)
+    say("case determinism")
+    a = fa.forward(q, k, v, causal=True)
+    b = fa.forward(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_empty_and_degenerate():
+    import torch
+    fa = _fa()
+    dev = "cuda"
+    q = torch.randn(1, 2, 5, 128, device=dev).to(torch.bfloat16)
+    k0 = torch.empty(1, 2, 0, 128, device=dev, dtype=torch.bfloat16)
+    say("case Nk = 0")
+    o, lse = fa.forward(q, k0, k0.clone())
+    torch.cuda.synchronize()
+    assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
+    say("case Nq = 0 and B = 0")
+    qe = torch.empty(1, 2, 0, 128, device=dev, dtype=torch.bfloat16)
+    k = torch.randn(1, 2, 7, 128, device=dev).to(torch.bfloat16)
+    o, lse = fa.forward(qe, k, k)
+    ob, lb = fa.forward(torch.empty(0, 2, 5, 128, device=dev, dtype=torch.bfloat16),
+                        torch.empty(0, 2, 7, 128, device=dev, dtype=torch.bfloat16),
+                        torch.empty(0, 2, 7, 128, device=dev, dtype=torch.bfloat16))
+    torch.cuda.synchronize()
+    assert o.numel() == 0 and ob.numel() == 0
+    say("case decode Nk = 0")
+    o, lse = fa.decode(q[:, :, :1].contiguous(), k0, k0.clone(), 4)
+    torch.cuda.synchronize()
+    assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
+
+
+def test_argument_errors_on_device():
+    import torch
+    fa = _fa()
+    q = torch.randn(1, 1, 8, 128, device="cuda").to(torch.bfloat16)
+    with pytest.raises(TypeError):
+        fa.forward(q.float(), q.float(), q.float())
+    buf = torch.zeros(1 * 1 * 8 * 128 + 8, device="cuda", dtype=torch.bfloat16)
+    mis = buf[1:1 + 8 * 128].view(1, 1, 8, 128)  # 2-byte offset: not 16-byte aligned
+    with pytest.raises(fa.FaError) as ei:
+        fa.forward(mis, q, q)
+    assert ei.value.status == 4
+    with pytest.raises(fa.FaError) as ei:
+        fa.forward(q, q, q, scale=-1.0)
+    assert ei.value.status == 7
+    small = fa.workspace_for(q[:, :, :1].contiguous(), 2)[:16]
+    with pytest.raises(fa.FaError) as ei:
+        fa.decode(q[:, :, :1].contiguous(), q, q, 2, workspace=small)
+    assert ei.value.status == 5
