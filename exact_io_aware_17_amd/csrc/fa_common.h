@@ -61,6 +61,39 @@ __device__ __forceinline__ int kappa(int r) { return (r & ~12) | ((r & 4) << 1) 
 
 __device__ __forceinline__ float wave_xor32(float x) { return __shfl_xor(x, 32, 64); }
 
+// max(x, x of lane ^ 32) with one v_permlane32_swap (no LDS round trip).
+__device__ __forceinline__ float max_with_lane_xor32(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// 32-bit LDS byte address of a __shared__ pointer.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(size_t)(__attribute__((address_space(3))) const void*)p;
+}
+
+// Direct global -> LDS copy of 16 bytes per lane: lane l's bytes land at LDS
+// byte `lds_base + 16 l` (lds_base must be wave-uniform). Issued through
+// inline assembly so that the compiler does not make every later LDS read
+// wait for these copies; callers wait with wait_vmcnt0() before the barrier
+// that publishes the data.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds_base) : "memory", "m0");
+}
+
+// Same copy with a wave-uniform 64-bit global base in SGPRs and a 32-bit
+// per-lane byte offset (no per-lane 64-bit address arithmetic).
+__device__ __forceinline__ void dma16_sbase(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds_base)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+__device__ __forceinline__ void wait_vmcnt0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 // Cooperative copy of a [rows x D] bf16 tile from global memory (row-major,
 // row stride D) into registers, 16 bytes per thread per step, then into LDS
 // (swizzled). Rows at or past `nvalid` read as zero and are never fetched.

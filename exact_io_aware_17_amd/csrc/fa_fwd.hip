@@ -1,53 +1,115 @@
 // bf16 attention forward (prefill) for gfx950.
 //
 // Algorithm: the FA2 loop of "Flash Attention on the 5090 in CUDA C++"
-// ("Flash Attention 2 algorithm" pseudocode): one workgroup owns one block of
+// ("Flash Attention 2 algorithm" pseudocode): a workgroup owns one block of
 // query rows of one (batch, head), zeroes its O tile, walks the KV tiles in
-// order, scores each tile, applies the online softmax and accumulates P.V, and
+// order, scores each tile, applies the online softmax, accumulates P.V and
 // stores O once. The online softmax is the running-max / running-denominator /
 // rescale recurrence of that page's "v1 -- basic version" bullets, kept in the
-// unnormalised form with one division at the end.
+// unnormalised form with a single division at the end.
 //
-// Mapping to CDNA4 (our design, not the page's sm120 one):
-//  * 256 threads = 4 waves; each wave owns 32 query rows, the workgroup 128.
-//  * Scores are computed transposed, S^T = K Q^T, with 32x32x16 bf16 MFMAs:
-//    the Q rows of the wave are the B operand and stay in registers for the
-//    whole KV loop; every lane then holds 32 scores of ONE query row, so the
-//    row max needs one cross-lane step (lane ^ 32) and the rescale factor is a
-//    per-lane scalar.
-//  * O is accumulated transposed, O^T += V^T P^T: the probabilities are already
-//    in B-operand layout (see kappa()), V^T comes from row-major LDS through
-//    transposing reads.
-//  * K/V tiles of 64 keys are double buffered in XOR-swizzled LDS; the next
-//    tile's global loads are in flight while the current tile is computed.
-//  * Causal: KV tiles past the workgroup's last visible key are never loaded;
-//    waves whose rows see nothing of a tile skip its math; only tiles that
-//    cross the diagonal (or the ragged end) are masked element-wise.
-//  * Workgroups are renumbered so that consecutive query blocks of one head
-//    land on the same XCD (shared L2 for that head's K/V); under the causal
+// Mapping to CDNA4 (our design; the page's sm120 kernel is prior art only):
+//  * 512 threads = 8 waves, two waves per SIMD. Waves 0-3 and 4-7 form two
+//    groups that own the same 128 query rows (32 rows per wave); group 0 takes
+//    the even KV tiles, group 1 the odd ones, and the two partial results are
+//    merged once at the end (same rescale, applied to the two halves).
+//  * Scores are computed transposed, S^T = K Q^T, with 32x32x16 bf16 MFMAs.
+//    The wave's Q rows are the B operand and stay in registers for the whole
+//    loop; every lane then holds the scores of ONE query row, so the row max
+//    needs one cross-lane step and the rescale factor is a per-lane scalar.
+//  * O is accumulated transposed, O^T += V^T P^T: the probabilities already
+//    sit in B-operand layout (kappa() in fa_common.h), V^T comes from the
+//    row-major LDS tile through transposing LDS reads.
+//  * Tiles of 64 keys go straight from global memory into XOR-swizzled LDS
+//    (global_load_lds, no register staging): four K slots and four V slots;
+//    loads for the tiles of the step after next are in flight while the
+//    current step computes. K runs one step ahead of V because each wave
+//    scores its next tile while it finishes the current one.
+//  * Software pipeline per wave: the score MFMAs of the wave's next tile are
+//    issued before the softmax of its current tile, so MFMA and VALU work of
+//    two tiles interleave.
+//  * Lazy rescale: the reference max m used in exp2(s - m) is raised only when
+//    a row's new max exceeds it by more than 8 (log2 units); until then the
+//    stale m keeps every exponent <= 2^8, which fp32 sums and bf16
+//    probabilities hold exactly as well. O and l are always scaled by the same
+//    factor, so the result is the same exact attention; the O rescale (64
+//    multiplies per lane) runs only on the rare tiles that raise m.
+//  * Causal: tiles past the workgroup's last visible key are never loaded; a
+//    wave skips the math of tiles its rows cannot see; only tiles that cross
+//    the diagonal or the ragged end are masked element-wise.
+//  * Workgroups are renumbered so that the query blocks of one head run on one
+//    XCD (its L2 then serves that head's K/V to all of them); under the causal
 //    mask the longest query blocks are issued first.
+#include <type_traits>
+
 #include "fa_common.h"
 #include "fa_internal.h"
 
 namespace fa {
 namespace {
 
-constexpr int kFwdThreads = 256;
+constexpr int kFwdThreads = 512;
 constexpr int kFwdBM = 128;
 constexpr int kFwdBN = 64;
+constexpr int kSlots = 4;
+constexpr float kLazyTau = 8.0f;
+
+template <int D>
+struct FwdLayout {
+  static constexpr int BN = kFwdBN;
+  static constexpr int TILE_BYTES = BN * D * 2;
+  static constexpr int V_BASE = kSlots * TILE_BYTES;  // V slots follow the K slots
+  static constexpr int CH = D / 8;                    // 16-byte chunks per row
+  static constexpr int ROWS_PER_KB = 64 / CH;         // rows one wave copy instruction covers
+  static constexpr int BLOCKS = BN * CH / 64;         // wave copy instructions per tile
+  static constexpr int NW = kFwdThreads / 64;
+  static constexpr int COPIES = BLOCKS / NW;          // copy instructions per wave per tile
+  static_assert(BLOCKS % NW == 0, "tile must split evenly over waves");
+};
+
+// Copy one K or V tile (BN rows x D) from global memory into an LDS slot with
+// direct-to-LDS copies. Each wave instruction writes 1 KiB of LDS, lane l at
+// byte 16 l; the swizzle is applied on the source side (`goff` holds, per copy
+// instruction, the byte offset of the global chunk whose swizzled position is
+// the lane's LDS position). A ragged last tile fetches row nvalid-1 in place
+// of the missing rows (finite data whose scores are masked and whose
+// probabilities are zero).
+template <int D>
+__device__ __forceinline__ void tile_to_lds(uint32_t slot_lds, const uint16_t* src, int nvalid,
+                                            const uint32_t (&goff)[FwdLayout<D>::COPIES], int wave, int lane) {
+  using L = FwdLayout<D>;
+  if (nvalid >= L::BN) {
+#pragma unroll
+    for (int i = 0; i < L::COPIES; ++i) dma16_sbase(src, goff[i], slot_lds + (wave + i * L::NW) * 1024);
+  } else {
+#pragma unroll
+    for (int i = 0; i < L::COPIES; ++i) {
+      const int blk = wave + i * L::NW;
+      const int row = blk * L::ROWS_PER_KB + lane / L::CH;
+      const int srow = row < nvalid ? row : nvalid - 1;
+      const uint32_t off = (uint32_t)(srow * D + swz<D>(row, lane % L::CH) * 8) * 2u;
+      dma16_sbase(src, off, slot_lds + blk * 1024);
+    }
+  }
+}
 
 template <int D>
 __global__ __launch_bounds__(kFwdThreads) void fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    uint16_t* __restrict__ O, float* __restrict__ LSE, int Hq, int Hkv, int Nq, int Nk,
-    float sl2, int causal, int n_qt, int n_wg) {
+    uint16_t* __restrict__ O, float* __restrict__ LSE, int Hq, int Hkv, int Nq, int Nk, float sl2, int causal,
+    int n_qt, int n_wg) {
+  using L = FwdLayout<D>;
   constexpr int BN = kFwdBN;
-  constexpr int KS = D / 16;  // k-steps of the score MFMA
-  constexpr int DB = D / 32;  // d blocks of the output
-  constexpr int MB = BN / 32; // 32-key blocks per tile
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2][2][BN * D];
+  constexpr int KS = D / 16;
+  constexpr int DB = D / 32;
+  constexpr int ROWB = D * 2;  // bytes per tile row
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * kSlots * BN * D];
+  const char* lds_c = reinterpret_cast<const char*>(lds);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2, rw = wave & 3;
+  const int hl = lane >> 5;  // half of the wave
 
   int wg = blockIdx.x;
   if ((n_wg & 7) == 0) wg = (wg & 7) * (n_wg >> 3) + (wg >> 3);
@@ -60,19 +122,44 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_bf16_kernel(
   const uint16_t* Kh = K + (size_t)(b * Hkv + g) * Nk * D;
   const uint16_t* Vh = V + (size_t)(b * Hkv + g) * Nk * D;
 
-  const int qw0 = qt * kFwdBM + wave * 32;
+  const int qw0 = qt * kFwdBM + rw * 32;
   const int qrow = qw0 + (lane & 31);
   const int diag = Nk - Nq;  // key j visible to row i iff j <= i + diag
 
   bf16x8 qf[KS];
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
-    if (qrow < Nq) {
-      qf[s] = *reinterpret_cast<const bf16x8*>(Qh + (size_t)qrow * D + s * 16 + (lane >> 5) * 8);
-    } else {
-      qf[s] = bf16x8{};
-    }
+    qf[s] = qrow < Nq ? *reinterpret_cast<const bf16x8*>(Qh + (size_t)qrow * D + s * 16 + hl * 8) : bf16x8{};
   }
+
+  // Loop-invariant per-lane LDS byte offsets (relative to `lds`). The group's
+  // slot (group g computes tiles with the parity of g, in slots g and 2 + g)
+  // is folded in; the tile's row block and the step parity are immediates.
+  uint32_t koff[KS];
+  {
+    const int row = kappa(lane & 31);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) koff[s] = grp * L::TILE_BYTES + row * ROWB + swz<D>(row, 2 * s + hl) * 16;
+  }
+  uint32_t voff[DB][2];
+  {
+    const int w = lane & 15, e = w >> 2, j = w & 3, q16 = (lane >> 4) & 1;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int row = hl * 8 + e + 4 * r;
+        const int ch = db * 4 + q16 * 2 + (j >> 1);
+        voff[db][r] = L::V_BASE + grp * L::TILE_BYTES + row * ROWB + swz<D>(row, ch) * 16 + (j & 1) * 8;
+      }
+  }
+  uint32_t goff[L::COPIES];
+#pragma unroll
+  for (int i = 0; i < L::COPIES; ++i) {
+    const int row = (wave + i * L::NW) * L::ROWS_PER_KB + lane / L::CH;
+    goff[i] = (uint32_t)(row * D + swz<D>(row, lane % L::CH) * 8) * 2u;
+  }
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(lds));
 
   int kv_end = Nk;
   if (causal) {
@@ -80,105 +167,155 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_bf16_kernel(
     kv_end = last < 0 ? 0 : (int)(last + 1 < (long)Nk ? last + 1 : Nk);
   }
   const int n_tiles = (kv_end + BN - 1) / BN;
+  // Tiles this wave's rows can see (visibility only shrinks with the tile index).
+  int n_vis = n_tiles;
+  if (causal) {
+    const long lastw = (long)qw0 + 31 + diag;
+    const long nv = lastw < 0 ? 0 : lastw / BN + 1;
+    n_vis = nv < n_tiles ? (int)nv : n_tiles;
+  }
 
   f32x16 o[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) o[db] = f32x16{};
   float m_run = kNegInf, l_run = 0.f;
 
-  TileCopy<D, BN, kFwdThreads> kc, vc;
-  if (n_tiles > 0) {
-    kc.load(Kh, Nk, tid);
-    vc.load(Vh, Nk, tid);
-    kc.store(smem[0][0], tid);
-    vc.store(smem[0][1], tid);
-  }
+  auto load_tile = [&](int t) {
+    const int slot = t % kSlots;
+    tile_to_lds<D>(lds0 + slot * L::TILE_BYTES, Kh + (size_t)t * BN * D, Nk - t * BN, goff, wave, lane);
+    tile_to_lds<D>(lds0 + L::V_BASE + slot * L::TILE_BYTES, Vh + (size_t)t * BN * D, Nk - t * BN, goff, wave,
+                   lane);
+  };
+
+  // Prologue: tiles 0 and 1.
+  for (int t = 0; t < 2 && t < n_tiles; ++t) load_tile(t);
+  wait_vmcnt0();
   __syncthreads();
 
-  for (int t = 0; t < n_tiles; ++t) {
-    const int kv0 = t * BN;
-    const bool has_next = t + 1 < n_tiles;
-    if (has_next) {
-      kc.load(Kh + (size_t)(kv0 + BN) * D, Nk - kv0 - BN, tid);
-      vc.load(Vh + (size_t)(kv0 + BN) * D, Nk - kv0 - BN, tid);
-    }
-    const uint16_t* ks = smem[t & 1][0];
-    const uint16_t* vs = smem[t & 1][1];
-    const bool wave_live = !causal || (kv0 <= qw0 + 31 + diag);
-    if (wave_live) {
-      f32x16 sacc[MB];
+  // One step computes tiles 2 step (group 0) and 2 step + 1 (group 1) from
+  // slots 2 (step & 1) + group, while tiles 2 step + 2, 2 step + 3 stream in.
+  auto step_body = [&](auto parity_c, int step) {
+    constexpr int PAR = decltype(parity_c)::value;
+    constexpr int PB = PAR * 2 * L::TILE_BYTES;  // parity part of the slot offset
+    const int t0 = 2 * step;
+    for (int t = t0 + 2; t < t0 + 4 && t < n_tiles; ++t) load_tile(t);
+
+    const int t = t0 + grp;
+    if (t < n_vis) {
+      const int kv0 = t * BN;
+      // S^T = K Q^T for the tile's two 32-key blocks.
+      f32x16 sc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        sacc[mb] = f32x16{};
-#pragma unroll
-        for (int s = 0; s < KS; ++s) sacc[mb] = mfma32(load_k_operand<D>(ks, mb * 32, s, lane), qf[s], sacc[mb]);
+      for (int s = 0; s < KS; ++s) {
+        const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(lds_c + koff[s] + PB);
+        const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(lds_c + koff[s] + PB + 32 * ROWB);
+        sc[0] = mfma32(a0, qf[s], sc[0]);
+        sc[1] = mfma32(a1, qf[s], sc[1]);
       }
       const bool need_mask = (kv0 + BN > Nk) || (causal && kv0 + BN - 1 > qw0 + diag);
       if (need_mask) {
         const int lim = causal ? qrow + diag : 0x7fffffff;
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
+        for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int key = kv0 + score_key(mb * 32, i, lane);
-            if (key >= Nk || key > lim) sacc[mb][i] = kNegInf;
+            if (key >= Nk || key > lim) sc[mb][i] = kNegInf;
           }
       }
       float mx = kNegInf;
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
+      for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[mb][i]);
-      mx = fmaxf(mx, wave_xor32(mx));
-      const float m_new = fmaxf(m_run, mx * sl2);
-      const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run - m_use);
-      float rs = 0.f;
-      bf16x8 p[MB][2];
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[mb][i]);
+      mx = max_with_lane_xor32(mx) * sl2;
+      if (__any(mx > m_run + kLazyTau)) {
+        const float m_new = fmaxf(m_run, mx);
+        // Rows that have seen no key yet keep m = -inf; their l and O are 0,
+        // and the base 0 keeps exp2(-inf - base) = 0 instead of NaN.
+        const float alpha = fast_exp2(m_run - (m_new == kNegInf ? 0.f : m_new));
+        l_run *= alpha;
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
+        for (int db = 0; db < DB; ++db) o[db] *= alpha;
+        m_run = m_new;
+      }
+      const float neg_m = m_run == kNegInf ? 0.f : -m_run;
+      float rs[4] = {0.f, 0.f, 0.f, 0.f};
+      bf16x8 p[2][2];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float e = fast_exp2(__builtin_fmaf(sacc[mb][i], sl2, -m_use));
-          rs += e;
+          const float e = fast_exp2(__builtin_fmaf(sc[mb][i], sl2, neg_m));
+          rs[i & 3] += e;
           p[mb][i >> 3][i & 7] = (__bf16)e;
         }
-      l_run = l_run * alpha + rs;
-      m_run = m_new;
+      l_run += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+      // O^T += V^T P^T.
 #pragma unroll
-      for (int db = 0; db < DB; ++db) o[db] *= alpha;
+      for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
+        for (int hf = 0; hf < 2; ++hf) {
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-          for (int db = 0; db < DB; ++db)
-            o[db] = mfma32(load_vt_operand<D>(vs, mb * 32 + hf * 16, db, lane), p[mb][hf], o[db]);
+          for (int db = 0; db < DB; ++db) {
+            const int kb = (mb * 32 + hf * 16) * ROWB;
+            const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(lds_c + voff[db][0] + PB + kb));
+            const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(lds_c + voff[db][1] + PB + kb));
+            o[db] = mfma32(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), p[mb][hf], o[db]);
+          }
+        }
     }
-    if (has_next) {
-      kc.store(smem[(t + 1) & 1][0], tid);
-      vc.store(smem[(t + 1) & 1][1], tid);
-    }
+    wait_vmcnt0();
     __syncthreads();
+  };
+
+  for (int step = 0; 2 * step < n_tiles; step += 2) {
+    step_body(std::integral_constant<int, 0>{}, step);
+    if (2 * (step + 1) >= n_tiles) break;
+    step_body(std::integral_constant<int, 1>{}, step + 1);
   }
 
-  // Epilogue: O = O~ / l, LSE = ln(2) * (m + log2 l); rows without keys: 0, -inf.
+  // Merge the two groups (same rows, disjoint key sets) and write out.
+  float* xo = reinterpret_cast<float*>(lds);                     // [4 rw][DB][16][64] fp32
+  float* xm = reinterpret_cast<float*>(lds) + 4 * DB * 16 * 64;  // [4 rw][64] m, then [4 rw][64] l
   const float l_tot = l_run + wave_xor32(l_run);
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  if (qrow < Nq) {
-    uint16_t* orow = O + ((size_t)bh * Nq + qrow) * D;
+  if (grp == 1) {
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const int d = db * 32 + i4 * 8 + (lane >> 5) * 4;
-        u32x2 w;
-        w[0] = pack_bf16x2(o[db][i4 * 4 + 0] * inv, o[db][i4 * 4 + 1] * inv);
-        w[1] = pack_bf16x2(o[db][i4 * 4 + 2] * inv, o[db][i4 * 4 + 3] * inv);
-        *reinterpret_cast<u32x2*>(orow + d) = w;
-      }
-    if (lane < 32) {
-      LSE[(size_t)bh * Nq + qrow] = l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : kNegInf;
+      for (int i = 0; i < 16; ++i) xo[((rw * DB + db) * 16 + i) * 64 + lane] = o[db][i];
+    xm[rw * 64 + lane] = m_run;
+    xm[256 + rw * 64 + lane] = l_tot;
+  }
+  __syncthreads();
+  if (grp == 0) {
+    const float m1 = xm[rw * 64 + lane];
+    const float l1 = xm[256 + rw * 64 + lane];
+    const float M = fmaxf(m_run, m1);
+    const float a0 = M == kNegInf ? 0.f : fast_exp2(m_run - M);
+    const float a1 = M == kNegInf ? 0.f : fast_exp2(m1 - M);
+    const float lsum = l_tot * a0 + l1 * a1;
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+    const float c0 = a0 * inv, c1 = a1 * inv;
+    if (qrow < Nq) {
+      uint16_t* orow = O + ((size_t)bh * Nq + qrow) * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int d = db * 32 + i4 * 8 + hl * 4;
+          float v[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int i = i4 * 4 + j;
+            v[j] = o[db][i] * c0 + xo[((rw * DB + db) * 16 + i) * 64 + lane] * c1;
+          }
+          u32x2 w;
+          w[0] = pack_bf16x2(v[0], v[1]);
+          w[1] = pack_bf16x2(v[2], v[3]);
+          *reinterpret_cast<u32x2*>(orow + d) = w;
+        }
+      if (lane < 32) LSE[(size_t)bh * Nq + qrow] = lsum > 0.f ? (M + fast_log2(lsum)) * kLn2 : kNegInf;
     }
   }
 }
