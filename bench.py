@@ -76,7 +76,7 @@ def device_inputs(w, device):
     return get(synth.TENSOR_Q, w.q_shape), get(synth.TENSOR_K, w.kv_shape), get(synth.TENSOR_V, w.kv_shape)
 
 
-def time_steps(step, steps, warmup):
+def time_steps(step, steps, warmup, min_warm_s=0.0):
     """W untimed steps, then exactly K timed steps. Returns (wall seconds,
     mean per-launch event milliseconds). Events are recorded on the stream the
     kernels run on (the current torch stream, which the binding passes down)."""
@@ -84,6 +84,12 @@ def time_steps(step, steps, warmup):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
+    # The GPU clock ramps under sustained load; warm-up steps plus at least
+    # min_warm_s of untimed work put the timed steps at the steady clock.
+    t_end = time.perf_counter() + min_warm_s
+    while time.perf_counter() < t_end:
+        step()
+        torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     t0 = time.perf_counter()
     for i in range(steps):
@@ -96,7 +102,7 @@ def time_steps(step, steps, warmup):
     return wall, ev_ms
 
 
-def bench_prefill(w, steps, warmup, device):
+def bench_prefill(w, steps, warmup, device, min_warm_s=0.2):
     import torch
     import exact_io_aware_17_amd as fa
     q, k, v = device_inputs(w, device)
@@ -105,12 +111,12 @@ def bench_prefill(w, steps, warmup, device):
 
     def step():
         fa.fa_fwd(q, k, v, o, lse, scale=w.scale, causal=w.causal)
-    wall, ev_ms = time_steps(step, steps, warmup)
+    wall, ev_ms = time_steps(step, steps, warmup, min_warm_s)
     return {"wall_s": wall, "ms_per_step": wall * 1e3 / steps, "kernel_ms": ev_ms,
             "tflops": w.flops() / (wall / steps) / 1e12, "kernel_tflops": w.flops() / (ev_ms * 1e-3) / 1e12}
 
 
-def bench_decode(w, steps, warmup, device):
+def bench_decode(w, steps, warmup, device, min_warm_s=0.2):
     """Each step reads a different copy of K/V (three copies rotate) so that no
     step finds its 2 GiB of K/V in the 256 MB last-level cache."""
     import torch
@@ -126,7 +132,7 @@ def bench_decode(w, steps, warmup, device):
         kk, vv = copies[it[0] % len(copies)]
         it[0] += 1
         fa.fa_fwd_splitkv(q, kk, vv, o, lse, w.num_splits, ws, scale=w.scale)
-    wall, ev_ms = time_steps(step, steps, warmup)
+    wall, ev_ms = time_steps(step, steps, warmup, min_warm_s)
     nbytes = w.algorithmic_bytes()
     return {"wall_s": wall, "ms_per_step": wall * 1e3 / steps, "kernel_ms": ev_ms,
             "gbs": nbytes / (wall / steps) / 1e9, "kernel_gbs": nbytes / (ev_ms * 1e-3) / 1e9}
@@ -175,8 +181,8 @@ def copy_calib(device, nbytes=1 << 30, steps=3):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--all", action="store_true", help="also time the other prefill workloads")
     ap.add_argument("--only", choices=["prefill", "decode"], default=None)
@@ -201,11 +207,11 @@ def main():
     wp = synth.WORKLOADS[PREFILL]
     wd = synth.WORKLOADS[DECODE]
     if args.only == "prefill":
-        r = bench_prefill(wp, args.steps, args.warmup, device)
+        r = bench_prefill(wp, args.steps, args.warmup, device, min_warm_s=0.0)
         print(json.dumps({"only": "prefill", **r}))
         return
     if args.only == "decode":
-        r = bench_decode(wd, args.steps, args.warmup, device)
+        r = bench_decode(wd, args.steps, args.warmup, device, min_warm_s=0.0)
         print(json.dumps({"only": "decode", **r}))
         return
 
