@@ -5,6 +5,8 @@
 //     A operand, lane l: row m = l % 32, k = (l / 32) * 8 + j   (8 bf16)
 //     B operand, lane l: col n = l % 32, k = (l / 32) * 8 + j   (8 bf16)
 //     C/D, lane l, register i: row (i / 4) * 8 + (l / 32) * 4 + (i % 4), col l % 32.
+//   v_mfma_f32_16x16x32_bf16: A lane l: row l % 16, k = (l / 16) * 8 + j;
+//     B lane l: col l % 16, same k; C/D lane l, register i: row (l / 16) * 4 + i, col l % 16.
 //   ds_read_tr16_b64: in each group of 16 lanes, output lane i, element e is
 //     element (i % 4) of the 8 bytes addressed by lane 4 * e + i / 4 of the group.
 //     Four lanes that address consecutive 8-byte pieces of one row give the
@@ -66,6 +68,17 @@ __device__ __forceinline__ float max_with_lane_xor32(float x) {
   const uint32_t u = __float_as_uint(x);
   const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// max(x, x of lane ^ 16) with one v_permlane16_swap.
+__device__ __forceinline__ float max_with_lane_xor16(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
 // 32-bit LDS byte address of a __shared__ pointer.

@@ -10,15 +10,19 @@
 // rescale the online softmax applies to tiles ("Flash Attention on the 5090
 // in CUDA C++", "v1 -- basic version"), now applied to whole chunks.
 //
-// Partial kernel, one workgroup per (chunk s, 32-row block, KV head g, batch b):
+// Partial kernel, one workgroup per (chunk s, 16-row block, KV head g, batch b):
 //  * the rows are the (query head in g's group, query index) pairs, so the
 //    Hq/Hkv query heads that share a KV head read each K/V byte once;
-//  * 256 threads = 4 waves; tiles of 128 keys are loaded cooperatively and
-//    each wave scores and accumulates its own 32 keys of the tile with the
-//    same transposed MFMA layout as the prefill kernel, keeping its own
-//    running (m, l, O);
-//  * the next tile's global loads are in flight during the current tile's math;
-//  * at the end the four waves' states are merged through LDS.
+//  * 256 threads = 4 waves; the chunk's keys are cut into 32-key blocks and
+//    wave w takes blocks w, w+4, ...; each wave streams its blocks with two
+//    blocks of K and V in flight in registers (about 32 KiB per wave), so a
+//    CU with two workgroups keeps ~256 KiB of loads outstanding;
+//  * 16x16x32 bf16 MFMAs (16 rows: a GQA group of 4 wastes less of the tile
+//    than a 32-row one): S^T = K Q^T with K straight from registers (each load
+//    instruction reads 64 contiguous bytes of 16 key rows), then
+//    O^T += V^T P^T with V^T read transposed from a wave-private LDS slice;
+//  * each wave keeps its own running (m, l, O); the four are merged through
+//    LDS at the end and the chunk's normalised O_s and LSE_s are written.
 #include "fa_common.h"
 #include "fa_internal.h"
 
@@ -26,119 +30,182 @@ namespace fa {
 namespace {
 
 constexpr int kSplitThreads = 256;
-constexpr int kSplitBN = 128;
-constexpr int kSplitRows = 32;
+constexpr int kSplitRows = 16;
+constexpr int kBlk = 32;  // keys per wave block
 
 template <int D>
-__global__ __launch_bounds__(kSplitThreads) void splitkv_partial_kernel(
+struct SplitStage {
+  bf16x8 k[2][D / 32];  // K, sub-block a/b, one 16-byte piece per k-step
+  u32x4 v[kBlk * D / 8 / 64];  // V rows, coalesced (16 bytes per lane per instruction)
+};
+
+// Key offset (within a 32-key block) of the K row lane i16 feeds to the A
+// operand of sub-block `sb`: sub-block a rows 4G'+i hold keys 8G'+i, sub-block
+// b rows hold keys 8G'+4+i. Each lane's score registers then cover 8
+// consecutive keys, the key-contiguous B operand of the P.V MFMA.
+__device__ __forceinline__ int blk_key(int i16, int sb) { return 8 * (i16 >> 2) + 4 * sb + (i16 & 3); }
+
+template <int D>
+__device__ __forceinline__ void load_stage(SplitStage<D>& st, const uint16_t* __restrict__ Kh,
+                                           const uint16_t* __restrict__ Vh, int kb, int k1, int lane) {
+  constexpr int KS = D / 32;
+  const int i16 = lane & 15, g4 = lane >> 4;
+#pragma unroll
+  for (int sb = 0; sb < 2; ++sb) {
+    int key = kb + blk_key(i16, sb);
+    key = key < k1 ? key : k1 - 1;
+    const uint16_t* row = Kh + (size_t)key * D + 8 * g4;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) st.k[sb][s] = *reinterpret_cast<const bf16x8*>(row + 32 * s);
+  }
+  constexpr int CH = D / 8, RPI = 64 / CH;
+#pragma unroll
+  for (int t = 0; t < kBlk * D / 8 / 64; ++t) {
+    int key = kb + t * RPI + lane / CH;
+    key = key < k1 ? key : k1 - 1;
+    st.v[t] = *reinterpret_cast<const u32x4*>(Vh + (size_t)key * D + (lane % CH) * 8);
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kSplitThreads, 2) void splitkv_partial_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     float* __restrict__ Opart, float* __restrict__ LSEpart, int Hq, int Hkv, int Nq, int Nk,
     float sl2, int causal, int S, int chunk) {
-  constexpr int KS = D / 16, DB = D / 32;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2][kSplitBN * D];
+  constexpr int KS = D / 32;    // k-steps of the score MFMA
+  constexpr int DB = D / 16;    // 16-wide d blocks of O
+  constexpr int CH = D / 8, RPI = 64 / CH, VI = kBlk * D / 8 / 64;
+  __shared__ __attribute__((aligned(1024))) uint16_t vlds[4][kBlk * D];  // one V block per wave
   __shared__ float ms[4][kSplitRows], ls[4][kSplitRows];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int i16 = lane & 15, g4 = lane >> 4;
   const int s = blockIdx.x % S, rb = blockIdx.x / S;
   const int g = blockIdx.y, b = blockIdx.z;
   const int G = Hq / Hkv, R = G * Nq;
-  const int r = rb * kSplitRows + (lane & 31);
+  const int r = rb * kSplitRows + i16;
   const bool rvalid = r < R;
   const int hh = rvalid ? r / Nq : 0, qi = rvalid ? r - hh * Nq : 0;
   const int head = g * G + hh;
   const int diag = Nk - Nq;
 
   bf16x8 qf[KS];
-  const uint16_t* qrow = Q + ((size_t)(b * Hq + head) * Nq + qi) * D;
+  {
+    const uint16_t* qrow = Q + ((size_t)(b * Hq + head) * Nq + qi) * D + 8 * g4;
 #pragma unroll
-  for (int k = 0; k < KS; ++k) {
-    qf[k] = rvalid ? *reinterpret_cast<const bf16x8*>(qrow + k * 16 + (lane >> 5) * 8) : bf16x8{};
+    for (int k = 0; k < KS; ++k) qf[k] = rvalid ? *reinterpret_cast<const bf16x8*>(qrow + 32 * k) : bf16x8{};
   }
 
   const long k0l = (long)s * chunk;
   const int k0 = k0l < Nk ? (int)k0l : Nk;
   const int k1 = (long)k0 + chunk < (long)Nk ? k0 + chunk : Nk;
-  const int n_tiles = (k1 - k0 + kSplitBN - 1) / kSplitBN;
+  const int nblk = (k1 - k0 + kBlk - 1) / kBlk;
+  const int nbw = nblk > wave ? (nblk - wave + 3) / 4 : 0;  // blocks of this wave
   const int lim = causal ? qi + diag : 0x7fffffff;
 
   const uint16_t* Kh = K + (size_t)(b * Hkv + g) * Nk * D;
   const uint16_t* Vh = V + (size_t)(b * Hkv + g) * Nk * D;
+  uint16_t* vw = vlds[wave];
+  const char* vw_c = reinterpret_cast<const char*>(vw);
 
-  f32x16 o[DB];
+  // Loop-invariant LDS offsets: V stores (row t*RPI + lane/CH, chunk lane%CH)
+  // and the transposed V^T operand reads.
+  uint32_t vst_off[VI];
 #pragma unroll
-  for (int db = 0; db < DB; ++db) o[db] = f32x16{};
+  for (int t = 0; t < VI; ++t) {
+    const int row = t * RPI + lane / CH;
+    vst_off[t] = (row * D + swz<D>(row, lane % CH) * 8) * 2;
+  }
+  uint32_t vtr_off[DB][2];
+  {
+    const int e = i16 >> 2, c = i16 & 3;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int row = 8 * g4 + 4 * h + e;
+        const int col = 16 * db + 4 * c;
+        vtr_off[db][h] = (row * D + swz<D>(row, col / 8) * 8 + (col & 7)) * 2;
+      }
+  }
+
+  f32x4 o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) o[db] = f32x4{};
   float m_run = kNegInf, l_run = 0.f;
 
-  TileCopy<D, kSplitBN, kSplitThreads> kc, vc;
-  if (n_tiles > 0) {
-    kc.load(Kh + (size_t)k0 * D, k1 - k0, tid);
-    vc.load(Vh + (size_t)k0 * D, k1 - k0, tid);
-  }
-  for (int t = 0; t < n_tiles; ++t) {
-    const int kv0 = k0 + t * kSplitBN;
-    __syncthreads();
-    kc.store(smem[0], tid);
-    vc.store(smem[1], tid);
-    __syncthreads();
-    if (t + 1 < n_tiles) {
-      kc.load(Kh + (size_t)(kv0 + kSplitBN) * D, k1 - kv0 - kSplitBN, tid);
-      vc.load(Vh + (size_t)(kv0 + kSplitBN) * D, k1 - kv0 - kSplitBN, tid);
+  SplitStage<D> st[2];
+  if (nbw > 0) load_stage<D>(st[0], Kh, Vh, k0 + kBlk * wave, k1, lane);
+  if (nbw > 1) load_stage<D>(st[1], Kh, Vh, k0 + kBlk * (wave + 4), k1, lane);
+
+  auto block = [&](SplitStage<D>& cur, int i) {
+    const int kb = k0 + kBlk * (wave + 4 * i);
+#pragma unroll
+    for (int t = 0; t < VI; ++t) *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(vw) + vst_off[t]) = cur.v[t];
+    f32x4 sc[2] = {f32x4{}, f32x4{}};
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+      sc[0] = mfma16(cur.k[0][k], qf[k], sc[0]);
+      sc[1] = mfma16(cur.k[1][k], qf[k], sc[1]);
     }
-    const int r0 = wave * 32;
-    if (kv0 + r0 < k1) {
-      f32x16 sacc = f32x16{};
+    if (i + 2 < nbw) load_stage<D>(cur, Kh, Vh, k0 + kBlk * (wave + 4 * (i + 2)), k1, lane);
+    if (kb + kBlk > k1 || causal) {
 #pragma unroll
-      for (int k = 0; k < KS; ++k) sacc = mfma32(load_k_operand<D>(smem[0], r0, k, lane), qf[k], sacc);
-      if (kv0 + r0 + 32 > k1 || causal) {
+      for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = kv0 + score_key(r0, i, lane);
-          if (key >= k1 || key > lim) sacc[i] = kNegInf;
+        for (int j = 0; j < 4; ++j) {
+          const int key = kb + 8 * g4 + 4 * sb + j;
+          if (key >= k1 || key > lim) sc[sb][j] = kNegInf;
         }
-      }
-      float mx = kNegInf;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[i]);
-      mx = fmaxf(mx, wave_xor32(mx));
-      const float m_new = fmaxf(m_run, mx * sl2);
-      const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run - m_use);
-      float rs = 0.f;
-      bf16x8 p[2];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float e = fast_exp2(__builtin_fmaf(sacc[i], sl2, -m_use));
-        rs += e;
-        p[i >> 3][i & 7] = (__bf16)e;
-      }
-      l_run = l_run * alpha + rs;
-      m_run = m_new;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) o[db] *= alpha;
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-          o[db] = mfma32(load_vt_operand<D>(smem[1], r0 + hf * 16, db, lane), p[hf], o[db]);
     }
+    float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                     fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+    mx = max_with_lane_xor32(max_with_lane_xor16(mx)) * sl2;
+    const float m_new = fmaxf(m_run, mx);
+    const float base = m_new == kNegInf ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - base);
+    bf16x8 p;
+    float rs = 0.f;
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float e = fast_exp2(__builtin_fmaf(sc[sb][j], sl2, -base));
+        rs += e;
+        p[4 * sb + j] = (__bf16)e;
+      }
+    l_run = l_run * alpha + rs;
+    m_run = m_new;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vw_c + vtr_off[db][0]));
+      const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vw_c + vtr_off[db][1]));
+      o[db] = mfma16(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), p, o[db] * alpha);
+    }
+  };
+  for (int i = 0; i < nbw; i += 2) {
+    block(st[0], i);
+    if (i + 1 >= nbw) break;
+    block(st[1], i + 1);
   }
 
   // Merge the four waves' (m, l, O~) through LDS.
+  float l_tot = l_run + __shfl_xor(l_run, 16, 64);
+  l_tot += __shfl_xor(l_tot, 32, 64);
   __syncthreads();
-  float* os = reinterpret_cast<float*>(&smem[0][0]);  // [4][32][D] fp32, fits in the tile buffers
-  const float l_tot = l_run + wave_xor32(l_run);
-  if (lane < 32) {
+  float* os = reinterpret_cast<float*>(&vlds[0][0]);  // [4][DB][4][64] fp32 (16 KiB per wave at D=128)
+  if (lane < kSplitRows) {
     ms[wave][lane] = m_run;
     ls[wave][lane] = l_tot;
   }
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int d = db * 32 + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
-      os[(wave * kSplitRows + (lane & 31)) * D + d] = o[db][i];
-    }
+    for (int i = 0; i < 4; ++i) os[((wave * DB + db) * 4 + i) * 64 + lane] = o[db][i];
   __syncthreads();
+  // Thread (row, d): row = idx / D, d = idx % D; O^T element (d, row) sits in
+  // register i = d % 4 of lane 16 * ((d % 16) / 4) + row, block d / 16.
   for (int idx = tid; idx < kSplitRows * D; idx += kSplitThreads) {
     const int row = idx / D, d = idx - row * D;
     const int rr = rb * kSplitRows + row;
@@ -150,11 +217,12 @@ __global__ __launch_bounds__(kSplitThreads) void splitkv_partial_kernel(
     float val = 0.f, lse = kNegInf;
     if (M != kNegInf) {
       float den = 0.f, num = 0.f;
+      const int src_lane = 16 * ((d & 15) >> 2) + row;
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         const float sc = fast_exp2(ms[w][row] - M);
         den += ls[w][row] * sc;
-        num += os[(w * kSplitRows + row) * D + d] * sc;
+        num += os[((w * DB + (d >> 4)) * 4 + (d & 3)) * 64 + src_lane] * sc;
       }
       val = num / den;
       lse = (M + fast_log2(den)) * kLn2;
