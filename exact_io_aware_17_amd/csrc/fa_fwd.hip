@@ -62,7 +62,7 @@ struct FwdLayout {
   static constexpr int CH = D / 8;                    // 16-byte chunks per row
   static constexpr int ROWS_PER_KB = 64 / CH;         // rows one wave copy instruction covers
   static constexpr int BLOCKS = BN * CH / 64;         // wave copy instructions per tile
-  static constexpr int NW = kFwdThreads / 64;
+  static constexpr int NW = 4;                        // the waves of group 0 issue all copies
   static constexpr int COPIES = BLOCKS / NW;          // copy instructions per wave per tile
   static_assert(BLOCKS % NW == 0, "tile must split evenly over waves");
 };
@@ -131,15 +131,19 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_bf16_kernel(
   for (int s = 0; s < KS; ++s) {
     qf[s] = qrow < Nq ? *reinterpret_cast<const bf16x8*>(Qh + (size_t)qrow * D + s * 16 + hl * 8) : bf16x8{};
   }
+  // Consume the Q loads here, before any tile copy is in flight: otherwise the
+  // compiler's wait for them lands inside the loop as a vmcnt(0) that would
+  // also wait for every outstanding tile copy.
+#pragma unroll
+  for (int s = 0; s < KS; ++s) asm volatile("" ::"v"(qf[s]));
 
-  // Loop-invariant per-lane LDS byte offsets (relative to `lds`). The group's
-  // slot (group g computes tiles with the parity of g, in slots g and 2 + g)
-  // is folded in; the tile's row block and the step parity are immediates.
+  // Loop-invariant per-lane LDS byte offsets (relative to `lds`); the slot
+  // and the tile's row block are immediates.
   uint32_t koff[KS];
   {
     const int row = kappa(lane & 31);
 #pragma unroll
-    for (int s = 0; s < KS; ++s) koff[s] = grp * L::TILE_BYTES + row * ROWB + swz<D>(row, 2 * s + hl) * 16;
+    for (int s = 0; s < KS; ++s) koff[s] = row * ROWB + swz<D>(row, 2 * s + hl) * 16;
   }
   uint32_t voff[DB][2];
   {
@@ -150,13 +154,13 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_bf16_kernel(
       for (int r = 0; r < 2; ++r) {
         const int row = hl * 8 + e + 4 * r;
         const int ch = db * 4 + q16 * 2 + (j >> 1);
-        voff[db][r] = L::V_BASE + grp * L::TILE_BYTES + row * ROWB + swz<D>(row, ch) * 16 + (j & 1) * 8;
+        voff[db][r] = L::V_BASE + row * ROWB + swz<D>(row, ch) * 16 + (j & 1) * 8;
       }
   }
   uint32_t goff[L::COPIES];
 #pragma unroll
   for (int i = 0; i < L::COPIES; ++i) {
-    const int row = (wave + i * L::NW) * L::ROWS_PER_KB + lane / L::CH;
+    const int row = (rw + i * L::NW) * L::ROWS_PER_KB + lane / L::CH;
     goff[i] = (uint32_t)(row * D + swz<D>(row, lane % L::CH) * 8) * 2u;
   }
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(lds));
@@ -180,99 +184,156 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_bf16_kernel(
   for (int db = 0; db < DB; ++db) o[db] = f32x16{};
   float m_run = kNegInf, l_run = 0.f;
 
-  auto load_tile = [&](int t) {
-    const int slot = t % kSlots;
-    tile_to_lds<D>(lds0 + slot * L::TILE_BYTES, Kh + (size_t)t * BN * D, Nk - t * BN, goff, wave, lane);
-    tile_to_lds<D>(lds0 + L::V_BASE + slot * L::TILE_BYTES, Vh + (size_t)t * BN * D, Nk - t * BN, goff, wave,
-                   lane);
+  auto load_k = [&](int t) __attribute__((always_inline)) {
+    tile_to_lds<D>(lds0 + (t % kSlots) * L::TILE_BYTES, Kh + (size_t)t * BN * D, Nk - t * BN, goff, rw, lane);
+  };
+  auto load_v = [&](int t) __attribute__((always_inline)) {
+    tile_to_lds<D>(lds0 + L::V_BASE + (t % kSlots) * L::TILE_BYTES, Vh + (size_t)t * BN * D, Nk - t * BN, goff,
+                   rw, lane);
   };
 
-  // Prologue: tiles 0 and 1.
-  for (int t = 0; t < 2 && t < n_tiles; ++t) load_tile(t);
-  wait_vmcnt0();
-  __syncthreads();
+  // Scores S^T = K Q^T of one tile (two 32-key blocks) from K slot offset KB.
+  auto score = [&](f32x16(&sc)[2], auto kb_c) __attribute__((always_inline)) {
+    constexpr int KB = decltype(kb_c)::value;
+    sc[0] = f32x16{};
+    sc[1] = f32x16{};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(lds_c + koff[s] + KB);
+      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(lds_c + koff[s] + KB + 32 * ROWB);
+      sc[0] = mfma32(a0, qf[s], sc[0]);
+      sc[1] = mfma32(a1, qf[s], sc[1]);
+    }
+  };
 
-  // One step computes tiles 2 step (group 0) and 2 step + 1 (group 1) from
-  // slots 2 (step & 1) + group, while tiles 2 step + 2, 2 step + 3 stream in.
-  auto step_body = [&](auto parity_c, int step) {
-    constexpr int PAR = decltype(parity_c)::value;
-    constexpr int PB = PAR * 2 * L::TILE_BYTES;  // parity part of the slot offset
-    const int t0 = 2 * step;
-    for (int t = t0 + 2; t < t0 + 4 && t < n_tiles; ++t) load_tile(t);
-
-    const int t = t0 + grp;
-    if (t < n_vis) {
-      const int kv0 = t * BN;
-      // S^T = K Q^T for the tile's two 32-key blocks.
-      f32x16 sc[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(lds_c + koff[s] + PB);
-        const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(lds_c + koff[s] + PB + 32 * ROWB);
-        sc[0] = mfma32(a0, qf[s], sc[0]);
-        sc[1] = mfma32(a1, qf[s], sc[1]);
-      }
-      const bool need_mask = (kv0 + BN > Nk) || (causal && kv0 + BN - 1 > qw0 + diag);
-      if (need_mask) {
-        const int lim = causal ? qrow + diag : 0x7fffffff;
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = kv0 + score_key(mb * 32, i, lane);
-            if (key >= Nk || key > lim) sc[mb][i] = kNegInf;
-          }
-      }
-      float mx = kNegInf;
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[mb][i]);
-      mx = max_with_lane_xor32(mx) * sl2;
-      if (__any(mx > m_run + kLazyTau)) {
-        const float m_new = fmaxf(m_run, mx);
-        // Rows that have seen no key yet keep m = -inf; their l and O are 0,
-        // and the base 0 keeps exp2(-inf - base) = 0 instead of NaN.
-        const float alpha = fast_exp2(m_run - (m_new == kNegInf ? 0.f : m_new));
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) o[db] *= alpha;
-        m_run = m_new;
-      }
-      const float neg_m = m_run == kNegInf ? 0.f : -m_run;
-      float rs[4] = {0.f, 0.f, 0.f, 0.f};
-      bf16x8 p[2][2];
+  // Online softmax of tile t's scores (mask, row max, lazy rescale, exp2,
+  // fp32 row sum, bf16 probabilities).
+  auto softmax = [&](f32x16(&sc)[2], bf16x8(&p)[2][2], int t) __attribute__((always_inline)) {
+    const int kv0 = t * BN;
+    const bool need_mask = (kv0 + BN > Nk) || (causal && kv0 + BN - 1 > qw0 + diag);
+    if (need_mask) {
+      const int lim = causal ? qrow + diag : 0x7fffffff;
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float e = fast_exp2(__builtin_fmaf(sc[mb][i], sl2, neg_m));
-          rs[i & 3] += e;
-          p[mb][i >> 3][i & 7] = (__bf16)e;
+          const int key = kv0 + score_key(mb * 32, i, lane);
+          if (key >= Nk || key > lim) sc[mb][i] = kNegInf;
         }
-      l_run += (rs[0] + rs[1]) + (rs[2] + rs[3]);
-      // O^T += V^T P^T.
+    }
+    // Row max as a tree of 3-input maxima.
+    float m8[8];
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+    for (int j = 0; j < 8; ++j) m8[j] = fmaxf(fmaxf(sc[j >> 2][(j & 3) * 4 + 0], sc[j >> 2][(j & 3) * 4 + 1]),
+                                             fmaxf(sc[j >> 2][(j & 3) * 4 + 2], sc[j >> 2][(j & 3) * 4 + 3]));
+    float mx = fmaxf(fmaxf(fmaxf(m8[0], m8[1]), fmaxf(m8[2], m8[3])), fmaxf(fmaxf(m8[4], m8[5]), fmaxf(m8[6], m8[7])));
+    mx = max_with_lane_xor32(mx) * sl2;
+    if (__any(mx > m_run + kLazyTau)) {
+      const float m_new = fmaxf(m_run, mx);
+      // Rows that have seen no key yet keep m = -inf; their l and O are 0,
+      // and the base 0 keeps exp2(-inf - base) = 0 instead of NaN.
+      const float alpha = fast_exp2(m_run - (m_new == kNegInf ? 0.f : m_new));
+      l_run *= alpha;
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
+      for (int db = 0; db < DB; ++db) o[db] *= alpha;
+      m_run = m_new;
+    }
+    const float neg_m = m_run == kNegInf ? 0.f : -m_run;
+    float rs[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            const int kb = (mb * 32 + hf * 16) * ROWB;
-            const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(lds_c + voff[db][0] + PB + kb));
-            const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(lds_c + voff[db][1] + PB + kb));
-            o[db] = mfma32(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), p[mb][hf], o[db]);
-          }
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float e = fast_exp2(__builtin_fmaf(sc[mb][i], sl2, neg_m));
+        rs[i & 3] += e;
+        p[mb][i >> 3][i & 7] = (__bf16)e;
+      }
+    l_run += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+  };
+
+  // O^T += V^T P^T from V slot offset VB.
+  auto pv = [&](const bf16x8(&p)[2][2], auto vb_c) __attribute__((always_inline)) {
+    constexpr int VB = decltype(vb_c)::value;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const int kb = (mb * 32 + hf * 16) * ROWB;
+          const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(lds_c + voff[db][0] + VB + kb));
+          const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(lds_c + voff[db][1] + VB + kb));
+          o[db] = mfma32(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), p[mb][hf], o[db]);
         }
+  };
+
+  // Prologue: K tiles 0, 1 and V tile 0. Only group 0 issues tile copies: the
+  // copy queue then never stalls group 1, which carries the longer phase chain.
+  if (grp == 0) {
+    if (n_tiles > 0) {
+      load_k(0);
+      load_v(0);
+    }
+    if (n_tiles > 1) load_k(1);
+  }
+  wait_vmcnt0();
+  __syncthreads();
+
+  // Ping-pong schedule. The two waves of a SIMD belong to different groups
+  // and run complementary phase orders within each step, so one issues MFMAs
+  // while the other runs the softmax VALU work:
+  //   group 0, step s: scores of tile 2s | softmax 2s | P.V 2s
+  //   group 1, step s: softmax 2s-1 | P.V 2s-1 | scores of tile 2s+1 (kept in
+  //                    registers across the barrier)
+  // Slots (tile t in K slot t % 4 and V slot t % 4): in step s the groups use
+  // K 2s, 2s+1 and V 2s, 2s-1 while K 2s+2, 2s+3 and V 2s+2, 2s+1 stream in;
+  // every slot is refilled one step after its last use.
+  f32x16 sc[2];
+  bf16x8 p[2][2];
+  auto step_body = [&](auto grp_c, auto par_c, int step) __attribute__((always_inline)) {
+    constexpr int GRP = decltype(grp_c)::value;
+    constexpr int PAR = decltype(par_c)::value;  // step parity
+    const int t0 = 2 * step;
+    if constexpr (GRP == 0) {
+      // Group 0 also issues the step's tile copies (K t0+2, t0+3; V t0+2,
+      // t0+1), while group 1 starts with its softmax.
+      if (t0 + 2 < n_tiles) load_k(t0 + 2);
+      if (t0 + 3 < n_tiles) load_k(t0 + 3);
+      if (t0 + 2 < n_tiles) load_v(t0 + 2);
+      if (t0 + 1 < n_tiles) load_v(t0 + 1);
+      if (t0 < n_vis) {
+        score(sc, std::integral_constant<int, 2 * PAR * L::TILE_BYTES>{});
+        __builtin_amdgcn_sched_barrier(0);
+        softmax(sc, p, t0);
+        __builtin_amdgcn_sched_barrier(0);
+        pv(p, std::integral_constant<int, 2 * PAR * L::TILE_BYTES>{});
+      }
+    } else {
+      if (step > 0 && t0 - 1 < n_vis) {
+        softmax(sc, p, t0 - 1);
+        __builtin_amdgcn_sched_barrier(0);
+        pv(p, std::integral_constant<int, (2 * (1 - PAR) + 1) * L::TILE_BYTES>{});
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (t0 + 1 < n_vis) score(sc, std::integral_constant<int, (2 * PAR + 1) * L::TILE_BYTES>{});
     }
     wait_vmcnt0();
     __syncthreads();
   };
 
-  for (int step = 0; 2 * step < n_tiles; step += 2) {
-    step_body(std::integral_constant<int, 0>{}, step);
-    if (2 * (step + 1) >= n_tiles) break;
-    step_body(std::integral_constant<int, 1>{}, step + 1);
+  // Each group runs its own copy of the loop; both execute the same number of
+  // steps and therefore the same barriers.
+  auto run = [&](auto grp_c) __attribute__((always_inline)) {
+    for (int step = 0; 2 * step <= n_tiles; step += 2) {
+      step_body(grp_c, std::integral_constant<int, 0>{}, step);
+      if (2 * (step + 1) > n_tiles) break;
+      step_body(grp_c, std::integral_constant<int, 1>{}, step + 1);
+    }
+  };
+  if (grp == 0) {
+    run(std::integral_constant<int, 0>{});
+  } else {
+    run(std::integral_constant<int, 1>{});
   }
 
   // Merge the two groups (same rows, disjoint key sets) and write out.
