@@ -204,6 +204,14 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_bf16_kernel(
       sc[0] = mfma32(a0, qf[s], sc[0]);
       sc[1] = mfma32(a1, qf[s], sc[1]);
     }
+    // Keep the K-operand reads KS ahead of the MFMAs that consume them.
+    __builtin_amdgcn_sched_group_barrier(0x100, KS, 0);
+#pragma unroll
+    for (int i = 0; i < KS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, KS, 0);
   };
 
   // Online softmax of tile t's scores (mask, row max, lazy rescale, exp2,
