@@ -64,17 +64,22 @@ __device__ __forceinline__ int kappa(int r) { return (r & ~12) | ((r & 4) << 1) 
 __device__ __forceinline__ float wave_xor32(float x) { return __shfl_xor(x, 32, 64); }
 
 // max(x, x of lane ^ 32) with one v_permlane32_swap (no LDS round trip).
+// Maximum that propagates NaN (IEEE 754-2019 maximum). Unlike fmaxf it needs
+// no canonicalising of MFMA results first, and gfx950 does three operands in
+// one v_maximum3_f32.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 __device__ __forceinline__ float max_with_lane_xor32(float x) {
   const uint32_t u = __float_as_uint(x);
   const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 // max(x, x of lane ^ 16) with one v_permlane16_swap.
 __device__ __forceinline__ float max_with_lane_xor16(float x) {
   const uint32_t u = __float_as_uint(x);
   const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 __device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {

@@ -230,14 +230,19 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_bf16_kernel(
         }
     }
     // Row max as a tree of 3-input maxima.
-    float m8[8];
+    float mt[11];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) m8[j] = fmaxf(fmaxf(sc[j >> 2][(j & 3) * 4 + 0], sc[j >> 2][(j & 3) * 4 + 1]),
-                                             fmaxf(sc[j >> 2][(j & 3) * 4 + 2], sc[j >> 2][(j & 3) * 4 + 3]));
-    float mx = fmaxf(fmaxf(fmaxf(m8[0], m8[1]), fmaxf(m8[2], m8[3])), fmaxf(fmaxf(m8[4], m8[5]), fmaxf(m8[6], m8[7])));
+    for (int j = 0; j < 10; ++j) {
+      const int i0 = 3 * j, i1 = 3 * j + 1, i2 = 3 * j + 2;
+      mt[j] = vmax(vmax(sc[i0 >> 4][i0 & 15], sc[i1 >> 4][i1 & 15]), sc[i2 >> 4][i2 & 15]);
+    }
+    mt[10] = vmax(sc[1][14], sc[1][15]);
+    const float u0 = vmax(vmax(mt[0], mt[1]), mt[2]), u1 = vmax(vmax(mt[3], mt[4]), mt[5]);
+    const float u2 = vmax(vmax(mt[6], mt[7]), mt[8]), u3 = vmax(mt[9], mt[10]);
+    float mx = vmax(vmax(u0, u1), vmax(u2, u3));
     mx = max_with_lane_xor32(mx) * sl2;
     if (__any(mx > m_run + kLazyTau)) {
-      const float m_new = fmaxf(m_run, mx);
+      const float m_new = vmax(m_run, mx);
       // Rows that have seen no key yet keep m = -inf; their l and O are 0,
       // and the base 0 keeps exp2(-inf - base) = 0 instead of NaN.
       const float alpha = fast_exp2(m_run - (m_new == kNegInf ? 0.f : m_new));

@@ -159,10 +159,10 @@ __global__ __launch_bounds__(kSplitThreads, 2) void splitkv_partial_kernel(
           if (key >= k1 || key > lim) sc[sb][j] = kNegInf;
         }
     }
-    float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
-                     fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+    float mx = vmax(vmax(vmax(sc[0][0], sc[0][1]), sc[0][2]),
+                    vmax(vmax(sc[0][3], sc[1][0]), vmax(vmax(sc[1][1], sc[1][2]), sc[1][3])));
     mx = max_with_lane_xor32(max_with_lane_xor16(mx)) * sl2;
-    const float m_new = fmaxf(m_run, mx);
+    const float m_new = vmax(m_run, mx);
     const float base = m_new == kNegInf ? 0.f : m_new;
     const float alpha = fast_exp2(m_run - base);
     bf16x8 p;
