@@ -22,12 +22,15 @@
 //    row-major LDS tile through transposing LDS reads.
 //  * Tiles of 64 keys go straight from global memory into XOR-swizzled LDS
 //    (global_load_lds, no register staging): four K slots and four V slots;
-//    loads for the tiles of the step after next are in flight while the
-//    current step computes. K runs one step ahead of V because each wave
-//    scores its next tile while it finishes the current one.
-//  * Software pipeline per wave: the score MFMAs of the wave's next tile are
-//    issued before the softmax of its current tile, so MFMA and VALU work of
-//    two tiles interleave.
+//    the copies for the next step are in flight while the current step
+//    computes.
+//  * Two-phase ping-pong between the two waves of each SIMD: in every phase
+//    one wave issues only MFMAs (P.V of its previous tile, then the scores of
+//    its next tile) while the other runs only the softmax VALU work, with a
+//    barrier between phases. A wave whose next instruction is an MFMA waiting
+//    for the busy matrix core holds up the SIMD's VALU issue, so mixing both
+//    kinds of work in both waves lets neither run at full rate; separating
+//    the roles per phase does.
 //  * Lazy rescale: the reference max m used in exp2(s - m) is raised only when
 //    a row's new max exceeds it by more than 8 (log2 units); until then the
 //    stale m keeps every exponent <= 2^8, which fp32 sums and bf16
@@ -280,27 +283,26 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_bf16_kernel(
         }
   };
 
-  // Prologue: K tiles 0, 1 and V tile 0. Only group 0 issues tile copies: the
-  // copy queue then never stalls group 1, which carries the longer phase chain.
-  if (grp == 0) {
-    if (n_tiles > 0) {
-      load_k(0);
-      load_v(0);
-    }
+  // Prologue: K tiles 0 and 1 (issued by group 1, which issues every copy:
+  // it does so in its VALU phase, where a stalled copy issue delays no MFMA).
+  if (grp == 1) {
+    if (n_tiles > 0) load_k(0);
     if (n_tiles > 1) load_k(1);
   }
   wait_vmcnt0();
   __syncthreads();
 
-  // Ping-pong schedule. The two waves of a SIMD belong to different groups
-  // and run complementary phase orders within each step, so one issues MFMAs
-  // while the other runs the softmax VALU work:
-  //   group 0, step s: scores of tile 2s | softmax 2s | P.V 2s
-  //   group 1, step s: softmax 2s-1 | P.V 2s-1 | scores of tile 2s+1 (kept in
-  //                    registers across the barrier)
-  // Slots (tile t in K slot t % 4 and V slot t % 4): in step s the groups use
-  // K 2s, 2s+1 and V 2s, 2s-1 while K 2s+2, 2s+3 and V 2s+2, 2s+1 stream in;
-  // every slot is refilled one step after its last use.
+  // Two-phase ping-pong. The two waves of a SIMD belong to different groups;
+  // in each phase one of them issues only MFMAs (and their LDS operand
+  // reads) while the other runs only VALU work (the softmax), and a barrier
+  // separates the phases:
+  //   step s   phase A              | phase B
+  //   group 0: P.V 2s-2, scores 2s  | softmax 2s
+  //   group 1: copies, softmax 2s-1 | P.V 2s-1, scores 2s+1
+  // Scores and probabilities stay in registers across the barriers. Tile t
+  // lives in K slot t % 4 and V slot t % 4; step s reads K 2s, 2s+1 and V 2s-2,
+  // 2s-1 while K 2s+2, 2s+3 and V 2s, 2s+1 stream in; every slot is refilled
+  // one step after its last use.
   f32x16 sc[2];
   bf16x8 p[2][2];
   auto step_body = [&](auto grp_c, auto par_c, int step) __attribute__((always_inline)) {
@@ -308,26 +310,19 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_bf16_kernel(
     constexpr int PAR = decltype(par_c)::value;  // step parity
     const int t0 = 2 * step;
     if constexpr (GRP == 0) {
-      // Group 0 also issues the step's tile copies (K t0+2, t0+3; V t0+2,
-      // t0+1), while group 1 starts with its softmax.
+      if (step > 0 && t0 - 2 < n_vis) pv(p, std::integral_constant<int, 2 * (1 - PAR) * L::TILE_BYTES>{});
+      if (t0 < n_vis) score(sc, std::integral_constant<int, 2 * PAR * L::TILE_BYTES>{});
+      __syncthreads();
+      if (t0 < n_vis) softmax(sc, p, t0);
+    } else {
       if (t0 + 2 < n_tiles) load_k(t0 + 2);
       if (t0 + 3 < n_tiles) load_k(t0 + 3);
-      if (t0 + 2 < n_tiles) load_v(t0 + 2);
+      if (t0 < n_tiles) load_v(t0);
       if (t0 + 1 < n_tiles) load_v(t0 + 1);
-      if (t0 < n_vis) {
-        score(sc, std::integral_constant<int, 2 * PAR * L::TILE_BYTES>{});
-        __builtin_amdgcn_sched_barrier(0);
-        softmax(sc, p, t0);
-        __builtin_amdgcn_sched_barrier(0);
-        pv(p, std::integral_constant<int, 2 * PAR * L::TILE_BYTES>{});
-      }
-    } else {
-      if (step > 0 && t0 - 1 < n_vis) {
-        softmax(sc, p, t0 - 1);
-        __builtin_amdgcn_sched_barrier(0);
-        pv(p, std::integral_constant<int, (2 * (1 - PAR) + 1) * L::TILE_BYTES>{});
-        __builtin_amdgcn_sched_barrier(0);
-      }
+      const bool prev = step > 0 && t0 - 1 < n_vis;
+      if (prev) softmax(sc, p, t0 - 1);
+      __syncthreads();
+      if (prev) pv(p, std::integral_constant<int, (2 * (1 - PAR) + 1) * L::TILE_BYTES>{});
       if (t0 + 1 < n_vis) score(sc, std::integral_constant<int, (2 * PAR + 1) * L::TILE_BYTES>{});
     }
     wait_vmcnt0();
@@ -335,11 +330,13 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_bf16_kernel(
   };
 
   // Each group runs its own copy of the loop; both execute the same number of
-  // steps and therefore the same barriers.
+  // steps (the last one finishes P.V of the last tiles) and so the same
+  // barriers.
+  const int last_step = (n_tiles + 1) / 2;
   auto run = [&](auto grp_c) __attribute__((always_inline)) {
-    for (int step = 0; 2 * step <= n_tiles; step += 2) {
+    for (int step = 0; step <= last_step; step += 2) {
       step_body(grp_c, std::integral_constant<int, 0>{}, step);
-      if (2 * (step + 1) > n_tiles) break;
+      if (step + 1 > last_step) break;
       step_body(grp_c, std::integral_constant<int, 1>{}, step + 1);
     }
   };

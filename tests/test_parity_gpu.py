@@ -38,6 +38,11 @@ SMALL = [
     synth.Workload("ragged_gqa", 2, 4, 2, 200, 333, 128),
     synth.Workload("ragged_gqa_causal", 2, 4, 2, 200, 333, 128, causal=True),
     synth.Workload("more_queries_than_keys_causal_d64", 1, 3, 1, 130, 70, 64, causal=True),
+    # Head dim 128, causal, Nq > Nk: the first workgroups see no key at all.
+    synth.Workload("more_queries_than_keys_causal_d128", 1, 3, 1, 300, 70, 128, causal=True, seed=5),
+    synth.Workload("whole_tiles_queries_over_keys_causal", 1, 2, 1, 200, 64, 128, causal=True, seed=6),
+    # Exactly one 32-key tile: the second key group has no tile.
+    synth.Workload("exactly_one_small_tile", 1, 2, 2, 64, 32, 128, seed=7),
     synth.Workload("one_query_one_key", 1, 1, 1, 1, 1, 128),
     synth.Workload("keys_below_one_tile", 1, 2, 2, 300, 17, 128),
     synth.Workload("square_causal_3_tiles", 1, 2, 2, 384, 384, 128, causal=True),
