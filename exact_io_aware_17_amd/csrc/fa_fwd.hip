@@ -283,8 +283,7 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_bf16_kernel(
         }
   };
 
-  // Prologue: K tiles 0 and 1 (issued by group 1, which issues every copy:
-  // it does so in its VALU phase, where a stalled copy issue delays no MFMA).
+  // Prologue: K tiles 0 and 1.
   if (grp == 1) {
     if (n_tiles > 0) load_k(0);
     if (n_tiles > 1) load_k(1);
@@ -296,13 +295,16 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_bf16_kernel(
   // in each phase one of them issues only MFMAs (and their LDS operand
   // reads) while the other runs only VALU work (the softmax), and a barrier
   // separates the phases:
-  //   step s   phase A              | phase B
-  //   group 0: P.V 2s-2, scores 2s  | softmax 2s
-  //   group 1: copies, softmax 2s-1 | P.V 2s-1, scores 2s+1
-  // Scores and probabilities stay in registers across the barriers. Tile t
-  // lives in K slot t % 4 and V slot t % 4; step s reads K 2s, 2s+1 and V 2s-2,
-  // 2s-1 while K 2s+2, 2s+3 and V 2s, 2s+1 stream in; every slot is refilled
-  // one step after its last use.
+  //   step s   phase A                           | phase B
+  //   group 0: P.V 2s-2, scores 2s                 | copy K 2s+3, V 2s+1; softmax 2s
+  //   group 1: copy K 2s+2, V 2s; softmax 2s-1     | P.V 2s-1, scores 2s+1
+  // Each group issues its copies at the start of its VALU phase (a copy costs
+  // the issuing wave some 50 cycles whatever it overlaps) and waits for them
+  // one phase before the other group reads them: group 1 at the end of the
+  // step, group 0 before the next mid-step barrier. Scores and probabilities
+  // stay in registers across the barriers. Tile t lives in K slot t % 4 and V
+  // slot t % 4; step s reads K 2s, 2s+1 and V 2s-2, 2s-1, and every slot is
+  // refilled one step after its last use.
   f32x16 sc[2];
   bf16x8 p[2][2];
   auto step_body = [&](auto grp_c, auto par_c, int step) __attribute__((always_inline)) {
@@ -312,26 +314,28 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_bf16_kernel(
     if constexpr (GRP == 0) {
       if (step > 0 && t0 - 2 < n_vis) pv(p, std::integral_constant<int, 2 * (1 - PAR) * L::TILE_BYTES>{});
       if (t0 < n_vis) score(sc, std::integral_constant<int, 2 * PAR * L::TILE_BYTES>{});
+      wait_vmcnt0();
       __syncthreads();
+      if (t0 + 3 < n_tiles) load_k(t0 + 3);
+      if (t0 + 1 < n_tiles) load_v(t0 + 1);
       if (t0 < n_vis) softmax(sc, p, t0);
+      __syncthreads();
     } else {
       if (t0 + 2 < n_tiles) load_k(t0 + 2);
-      if (t0 + 3 < n_tiles) load_k(t0 + 3);
       if (t0 < n_tiles) load_v(t0);
-      if (t0 + 1 < n_tiles) load_v(t0 + 1);
       const bool prev = step > 0 && t0 - 1 < n_vis;
       if (prev) softmax(sc, p, t0 - 1);
       __syncthreads();
       if (prev) pv(p, std::integral_constant<int, (2 * (1 - PAR) + 1) * L::TILE_BYTES>{});
       if (t0 + 1 < n_vis) score(sc, std::integral_constant<int, (2 * PAR + 1) * L::TILE_BYTES>{});
+      wait_vmcnt0();
+      __syncthreads();
     }
-    wait_vmcnt0();
-    __syncthreads();
   };
 
   // Each group runs its own copy of the loop; both execute the same number of
   // steps (the last one finishes P.V of the last tiles) and so the same
-  // barriers.
+  // barriers. Group 0's copies of the last step are waited for below.
   const int last_step = (n_tiles + 1) / 2;
   auto run = [&](auto grp_c) __attribute__((always_inline)) {
     for (int step = 0; step <= last_step; step += 2) {
@@ -345,6 +349,8 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_bf16_kernel(
   } else {
     run(std::integral_constant<int, 1>{});
   }
+  wait_vmcnt0();
+  __syncthreads();
 
   // Merge the two groups (same rows, disjoint key sets) and write out.
   float* xo = reinterpret_cast<float*>(lds);                     // [4 rw][DB][16][64] fp32
