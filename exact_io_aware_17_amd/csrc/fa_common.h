@@ -75,6 +75,13 @@ __device__ __forceinline__ float max_with_lane_xor32(float x) {
   return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+// x + x of lane ^ 32 with one v_permlane32_swap; the same value in both lanes.
+__device__ __forceinline__ float sum_with_lane_xor32(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // max(x, x of lane ^ 16) with one v_permlane16_swap.
 __device__ __forceinline__ float max_with_lane_xor16(float x) {
   const uint32_t u = __float_as_uint(x);

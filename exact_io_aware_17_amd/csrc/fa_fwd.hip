@@ -31,12 +31,13 @@
 //    for the busy matrix core holds up the SIMD's VALU issue, so mixing both
 //    kinds of work in both waves lets neither run at full rate; separating
 //    the roles per phase does.
-//  * Lazy rescale: the reference max m used in exp2(s - m) is raised only when
-//    a row's new max exceeds it by more than 8 (log2 units); until then the
-//    stale m keeps every exponent <= 2^8, which fp32 sums and bf16
-//    probabilities hold exactly as well. O and l are always scaled by the same
-//    factor, so the result is the same exact attention; the O rescale (64
-//    multiplies per lane) runs only on the rare tiles that raise m.
+//  * Guarded reference instead of a per-tile row max: exp2(s - m) is taken
+//    against a row reference m (the true max of the row's first tile with a
+//    visible key) that only has to keep the tile's row sum at or below 2^64
+//    (checked on the row sum the softmax computes anyway); O and l always
+//    carry the same factor, so the result is the same exact attention. The
+//    row max, the new reference and the O rescale run only on a row's first
+//    tile and on the rare tiles that fail the check.
 //  * Causal: tiles past the workgroup's last visible key are never loaded; a
 //    wave skips the math of tiles its rows cannot see; only tiles that cross
 //    the diagonal or the ragged end are masked element-wise.
@@ -55,7 +56,8 @@ constexpr int kFwdThreads = 512;
 constexpr int kFwdBM = 128;
 constexpr int kFwdBN = 64;
 constexpr int kSlots = 4;
-constexpr float kLazyTau = 8.0f;
+// Largest row sum of one tile the softmax's common path accepts (see softmax).
+constexpr float kSumHi = 18446744073709551616.0f;  // 2^64
 
 template <int D>
 struct FwdLayout {
@@ -185,7 +187,7 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_bf16_kernel(
   f32x16 o[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) o[db] = f32x16{};
-  float m_run = kNegInf, l_run = 0.f;
+  float m_run = 0.f, l_run = 0.f;  // row reference (log2 units) and row sum
 
   auto load_k = [&](int t) __attribute__((always_inline)) {
     tile_to_lds<D>(lds0 + (t % kSlots) * L::TILE_BYTES, Kh + (size_t)t * BN * D, Nk - t * BN, goff, rw, lane);
@@ -217,8 +219,19 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_bf16_kernel(
     __builtin_amdgcn_sched_group_barrier(0x008, KS, 0);
   };
 
-  // Online softmax of tile t's scores (mask, row max, lazy rescale, exp2,
-  // fp32 row sum, bf16 probabilities).
+  // Online softmax of tile t's scores: mask, exp2 against the row's reference
+  // m, fp32 row sums, bf16 probabilities. The reference need not be the
+  // running max: any m at or below it that keeps every exp2(s - m) of the
+  // tile at or below 2^64 gives the same exact result (O and l always carry
+  // the same factor), with the same relative precision, and no fp32 or bf16
+  // overflow. So the common path does not compute the row max at all; it
+  // checks the tile's row sum instead. The rare path (row max, new reference,
+  // rescale of O and l, exponentials again) runs on a row's first tile with a
+  // visible key, which sets the reference to that tile's true max (the
+  // largest probability of a row whose keys all lie in one tile is then
+  // exactly 1), and when the scores jump by tens of binary orders. The row sum l_run
+  // holds the total of both halves of the row (lanes l and l ^ 32) in both
+  // lanes, so both halves always take the same decisions.
   auto softmax = [&](f32x16(&sc)[2], bf16x8(&p)[2][2], int t) __attribute__((always_inline)) {
     const int kv0 = t * BN;
     const bool need_mask = (kv0 + BN > Nk) || (causal && kv0 + BN - 1 > qw0 + diag);
@@ -232,39 +245,46 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_bf16_kernel(
           if (key >= Nk || key > lim) sc[mb][i] = kNegInf;
         }
     }
-    // Row max as a tree of 3-input maxima.
-    float mt[11];
+    // Probabilities against the current reference; returns the tile's row sum.
+    auto exps = [&]() __attribute__((always_inline)) {
+      const float neg_m = -m_run;
+      float rs[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < 10; ++j) {
-      const int i0 = 3 * j, i1 = 3 * j + 1, i2 = 3 * j + 2;
-      mt[j] = vmax(vmax(sc[i0 >> 4][i0 & 15], sc[i1 >> 4][i1 & 15]), sc[i2 >> 4][i2 & 15]);
-    }
-    mt[10] = vmax(sc[1][14], sc[1][15]);
-    const float u0 = vmax(vmax(mt[0], mt[1]), mt[2]), u1 = vmax(vmax(mt[3], mt[4]), mt[5]);
-    const float u2 = vmax(vmax(mt[6], mt[7]), mt[8]), u3 = vmax(mt[9], mt[10]);
-    float mx = vmax(vmax(u0, u1), vmax(u2, u3));
-    mx = max_with_lane_xor32(mx) * sl2;
-    if (__any(mx > m_run + kLazyTau)) {
-      const float m_new = vmax(m_run, mx);
-      // Rows that have seen no key yet keep m = -inf; their l and O are 0,
-      // and the base 0 keeps exp2(-inf - base) = 0 instead of NaN.
-      const float alpha = fast_exp2(m_run - (m_new == kNegInf ? 0.f : m_new));
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float e = fast_exp2(__builtin_fmaf(sc[mb][i], sl2, neg_m));
+          rs[i & 3] += e;
+          p[mb][i >> 3][i & 7] = (__bf16)e;
+        }
+      return sum_with_lane_xor32((rs[0] + rs[1]) + (rs[2] + rs[3]));
+    };
+    float tot = exps();
+    if (__any(!(tot <= kSumHi) || l_run == 0.f)) {
+      // Row max as a tree of 3-input maxima.
+      float mt[11];
+#pragma unroll
+      for (int j = 0; j < 10; ++j) {
+        const int i0 = 3 * j, i1 = 3 * j + 1, i2 = 3 * j + 2;
+        mt[j] = vmax(vmax(sc[i0 >> 4][i0 & 15], sc[i1 >> 4][i1 & 15]), sc[i2 >> 4][i2 & 15]);
+      }
+      mt[10] = vmax(sc[1][14], sc[1][15]);
+      const float u0 = vmax(vmax(mt[0], mt[1]), mt[2]), u1 = vmax(vmax(mt[3], mt[4]), mt[5]);
+      const float u2 = vmax(vmax(mt[6], mt[7]), mt[8]), u3 = vmax(mt[9], mt[10]);
+      const float mx = max_with_lane_xor32(vmax(vmax(u0, u1), vmax(u2, u3))) * sl2;
+      // New reference: the running max, or this tile's max while the row has
+      // accumulated nothing yet (l_run is then exactly 0, and so is O). A row
+      // with no visible key yet keeps its reference.
+      float m_new = l_run == 0.f ? mx : vmax(m_run, mx);
+      if (!(m_new > kNegInf)) m_new = m_run;
+      const float alpha = l_run == 0.f ? 1.f : fast_exp2(m_run - m_new);
       l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < DB; ++db) o[db] *= alpha;
       m_run = m_new;
+      tot = exps();
     }
-    const float neg_m = m_run == kNegInf ? 0.f : -m_run;
-    float rs[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float e = fast_exp2(__builtin_fmaf(sc[mb][i], sl2, neg_m));
-        rs[i & 3] += e;
-        p[mb][i >> 3][i & 7] = (__bf16)e;
-      }
-    l_run += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+    l_run += tot;
   };
 
   // O^T += V^T P^T from V slot offset VB.
@@ -355,7 +375,7 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_bf16_kernel(
   // Merge the two groups (same rows, disjoint key sets) and write out.
   float* xo = reinterpret_cast<float*>(lds);                     // [4 rw][DB][16][64] fp32
   float* xm = reinterpret_cast<float*>(lds) + 4 * DB * 16 * 64;  // [4 rw][64] m, then [4 rw][64] l
-  const float l_tot = l_run + wave_xor32(l_run);
+  const float l_tot = l_run;  // already the total of both lane halves
   if (grp == 1) {
 #pragma unroll
     for (int db = 0; db < DB; ++db)

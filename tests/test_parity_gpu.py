@@ -222,6 +222,37 @@ def test_structured_inputs():
     assert np.max(np.abs(o.float().cpu().numpy() - 1.0)) <= 8e-3
 
 
+@pytest.mark.parametrize("d,causal", [(128, False), (128, True), (64, False)])
+def test_logit_ramps(d, causal):
+    """Logits that rise, fall or stay flat across 32 key tiles (plus noise),
+    spanning far more than the fp32 exponent range within one row: rising rows
+    make the kernel move its exponent reference several times after rows have
+    accumulated large sums, falling rows drive later tiles to underflow.
+    Compared with the fp64 oracle on every row."""
+    import torch
+    fa = _fa()
+    r = np.random.default_rng(11)
+    Nq, Nk = 96, 2048
+    # s_ij = a_i t_j + b_i u_j (scale 1): t is a ramp over the keys, u noise.
+    t = np.linspace(-1.0, 1.0, Nk) * 90.0
+    u = r.standard_normal(Nk) * 2.0
+    k = np.zeros((1, 1, Nk, d))
+    k[0, 0, :, 0] = t
+    k[0, 0, :, 1] = u
+    q = np.zeros((1, 1, Nq, d))
+    q[0, 0, :, 0] = np.concatenate([np.linspace(0.2, 2.0, Nq // 3), -np.linspace(0.2, 2.0, Nq // 3),
+                                    np.zeros(Nq - 2 * (Nq // 3))])
+    q[0, 0, :, 1] = r.standard_normal(Nq)
+    v = r.standard_normal((1, 1, Nk, d))
+    qb, kb, vb = (_bf16_dev(x) for x in (q, k, v))
+    say(f"case logit ramps d={d} causal={causal}")
+    o, lse = fa.forward(qb, kb, vb, scale=1.0, causal=causal)
+    torch.cuda.synchronize()
+    to64 = lambda x: x.float().cpu().numpy().astype(np.float64)
+    o_ref, lse_ref = oracle.attention(to64(qb), to64(kb), to64(vb), 1.0, causal)
+    assert_close(errors(o.float().cpu().numpy(), o_ref, lse.cpu().numpy(), lse_ref), what=f"ramps d={d} causal={causal}")
+
+
 def test_gqa_equals_repeated_kv():
     import torch
     fa = _fa()
