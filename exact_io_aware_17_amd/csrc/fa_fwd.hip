@@ -27,10 +27,10 @@
 //  * Two-phase ping-pong between the two waves of each SIMD: in every phase
 //    one wave issues only MFMAs (P.V of its previous tile, then the scores of
 //    its next tile) while the other runs only the softmax VALU work, with a
-//    barrier between phases. A wave whose next instruction is an MFMA waiting
-//    for the busy matrix core holds up the SIMD's VALU issue, so mixing both
-//    kinds of work in both waves lets neither run at full rate; separating
-//    the roles per phase does.
+//    barrier between phases. The matrix core of each SIMD is fed by one wave
+//    (MFMAs and their LDS operand reads) while its VALU runs the other
+//    wave's softmax; a single wave doing both stalls its in-order stream on
+//    operand-read waits and copy issue.
 //  * Guarded reference instead of a per-tile row max: exp2(s - m) is taken
 //    against a row reference m (the true max of the row's first tile with a
 //    visible key) that only has to keep the tile's row sum at or below 2^64
