@@ -233,6 +233,10 @@ __global__ __launch_bounds__(kSplitThreads, 2) void splitkv_partial_kernel(
   }
 }
 
+// One wave per output row. With at most 64 chunks every lane reads one
+// chunk's LSE, so the max and the weights need no serial loop over chunks;
+// the O rows of four chunks are then loaded together per step. More chunks
+// take the plain loop.
 template <int D>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ Opart,
                                                       const float* __restrict__ LSEpart,
@@ -246,18 +250,50 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   const int qi = (int)(row - bh * Nq);
   const float* lp = LSEpart + (size_t)bh * S * Nq + qi;
   const float* op = Opart + ((size_t)bh * S * Nq + qi) * D + lane * PER;
-  float M = kNegInf;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, lp[(size_t)s * Nq]);
+  const size_t ostride = (size_t)Nq * D;
+  float M = kNegInf, den = 0.f;
   float acc[PER];
 #pragma unroll
   for (int p = 0; p < PER; ++p) acc[p] = 0.f;
-  float den = 0.f;
-  if (M != kNegInf) {
-    for (int s = 0; s < S; ++s) {
-      const float w = expf(lp[(size_t)s * Nq] - M);
-      den += w;
+  if (S <= 64) {
+    const float ls = lane < S ? lp[(size_t)lane * Nq] : kNegInf;
+    M = ls;
 #pragma unroll
-      for (int p = 0; p < PER; ++p) acc[p] = __builtin_fmaf(w, op[(size_t)s * Nq * D + p], acc[p]);
+    for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, __shfl_xor(M, m, 64));
+    const float w = (lane < S && M != kNegInf) ? expf(ls - M) : 0.f;
+    den = w;
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) den += __shfl_xor(den, m, 64);
+    if (M != kNegInf) {
+      int s = 0;
+      for (; s + 4 <= S; s += 4) {
+        float v[4][PER], ww[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          ww[j] = __shfl(w, s + j, 64);
+#pragma unroll
+          for (int p = 0; p < PER; ++p) v[j][p] = op[(size_t)(s + j) * ostride + p];
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int p = 0; p < PER; ++p) acc[p] = __builtin_fmaf(ww[j], v[j][p], acc[p]);
+      }
+      for (; s < S; ++s) {
+        const float ws = __shfl(w, s, 64);
+#pragma unroll
+        for (int p = 0; p < PER; ++p) acc[p] = __builtin_fmaf(ws, op[(size_t)s * ostride + p], acc[p]);
+      }
+    }
+  } else {
+    for (int s = 0; s < S; ++s) M = fmaxf(M, lp[(size_t)s * Nq]);
+    if (M != kNegInf) {
+      for (int s = 0; s < S; ++s) {
+        const float w = expf(lp[(size_t)s * Nq] - M);
+        den += w;
+#pragma unroll
+        for (int p = 0; p < PER; ++p) acc[p] = __builtin_fmaf(w, op[(size_t)s * ostride + p], acc[p]);
+      }
     }
   }
   const float inv = den > 0.f ? 1.f / den : 0.f;

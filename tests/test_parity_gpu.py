@@ -155,12 +155,14 @@ def test_decode_edge_cases(w):
     assert_close(errors(op, op_ref, lp, lp_ref), what=w.name + " partials")
 
 
-def test_combine_entry_point():
-    """fa_combine alone, on seeded random partials (some chunks empty)."""
+@pytest.mark.parametrize("S,d", [(5, 128), (64, 128), (100, 128), (7, 64), (70, 64)])
+def test_combine_entry_point(S, d):
+    """fa_combine alone, on seeded random partials (some chunks empty); up to
+    64 chunks take the lane-parallel path, more the plain loop."""
     import torch
     fa = _fa()
-    r = np.random.default_rng(5)
-    B, Hq, S, Nq, d = 2, 3, 5, 4, 128
+    r = np.random.default_rng(5 + S)
+    B, Hq, Nq = 2, 3, 4
     op = r.standard_normal((B, Hq, S, Nq, d)).astype(np.float32)
     lp = (r.standard_normal((B, Hq, S, Nq)) * 3).astype(np.float32)
     lp[0, 0, 1] = -np.inf
