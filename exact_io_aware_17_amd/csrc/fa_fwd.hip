@@ -136,11 +136,6 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_bf16_kernel(
   for (int s = 0; s < KS; ++s) {
     qf[s] = qrow < Nq ? *reinterpret_cast<const bf16x8*>(Qh + (size_t)qrow * D + s * 16 + hl * 8) : bf16x8{};
   }
-  // Consume the Q loads here, before any tile copy is in flight: otherwise the
-  // compiler's wait for them lands inside the loop as a vmcnt(0) that would
-  // also wait for every outstanding tile copy.
-#pragma unroll
-  for (int s = 0; s < KS; ++s) asm volatile("" ::"v"(qf[s]));
 
   // Loop-invariant per-lane LDS byte offsets (relative to `lds`); the slot
   // and the tile's row block are immediates.
@@ -303,12 +298,17 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_bf16_kernel(
         }
   };
 
-  // Prologue: K tiles 0 and 1.
+  // Prologue: K tiles 0 and 1, in flight together with the Q loads. The Q
+  // registers are consumed right after the common wait, so that the
+  // compiler's own wait for them (which would also wait for every tile copy
+  // in flight) is placed here and not inside the loop.
   if (grp == 1) {
     if (n_tiles > 0) load_k(0);
     if (n_tiles > 1) load_k(1);
   }
   wait_vmcnt0();
+#pragma unroll
+  for (int s = 0; s < KS; ++s) asm volatile("" ::"v"(qf[s]));
   __syncthreads();
 
   // Two-phase ping-pong. The two waves of a SIMD belong to different groups;
