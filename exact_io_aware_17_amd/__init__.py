@@ -5,12 +5,13 @@ library's HIP kernels. torch supplies device memory and streams. If the library
 is not built, loading it raises; there is no fallback path.
 
 Entry points with the C names (tensors in, status checked, nothing returned):
-    fa_fwd, fa_fwd_fp32, fa_fwd_splitkv, fa_combine, fa_splitkv_workspace_bytes,
-    fa_status_str
+    fa_fwd, fa_fwd_fp32, fa_fwd_splitkv, fa_fwd_splitkv_paged, fa_combine,
+    fa_splitkv_workspace_bytes, fa_status_str
 Convenience wrappers that allocate the outputs:
     forward(q, k, v, causal=False, scale=None)            -> (o, lse)
     forward_fp32(q, k, v, causal=False, scale=None)       -> (o, lse)
     decode(q, k, v, num_splits, causal=False, scale=None, workspace=None) -> (o, lse)
+    decode_paged(q, k_cache, v_cache, block_table, seq_lens, num_splits, ...) -> (o, lse)
 """
 from __future__ import annotations
 
@@ -33,6 +34,8 @@ SIGNATURES = {
     "fa_splitkv_workspace_bytes": (_S, [_I, _I, _I, _I, _I]),
     "fa_fwd_splitkv": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _P, _S, _P]),
     "fa_combine": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
+    "fa_fwd_splitkv_paged": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _I, _I, _P, _S,
+                                  _P]),
     "fa_status_str": (ctypes.c_char_p, [_I]),
 }
 
@@ -151,6 +154,34 @@ def fa_fwd_splitkv(q, k, v, o, lse, num_splits, workspace, scale=None, causal=Fa
     _check("fa_fwd_splitkv", st)
 
 
+def fa_fwd_splitkv_paged(q, k_cache, v_cache, block_table, seq_lens, o, lse, num_splits, workspace, scale=None,
+                         causal=False, stream=None):
+    """Split-KV forward over a paged cache: k_cache / v_cache bf16 [num_pages, Hkv, page_size, d],
+    block_table int32 [B, max_pages], seq_lens int32 [B] (all on the GPU)."""
+    import torch
+    if q.dtype != torch.bfloat16 or q.dim() != 4 or not q.is_contiguous() or q.device.type != "cuda":
+        raise ValueError("q must be a contiguous bf16 [B, Hq, Nq, d] GPU tensor")
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        if t.dtype != torch.bfloat16 or t.dim() != 4 or not t.is_contiguous() or t.device != q.device:
+            raise ValueError(f"{name} must be a contiguous bf16 [num_pages, Hkv, page_size, d] tensor on q's device")
+    if k_cache.shape != v_cache.shape:
+        raise ValueError("k_cache and v_cache shapes disagree")
+    for name, t in (("block_table", block_table), ("seq_lens", seq_lens)):
+        if t.dtype != torch.int32 or not t.is_contiguous() or t.device != q.device:
+            raise ValueError(f"{name} must be a contiguous int32 tensor on q's device")
+    B, Hq, Nq, d = q.shape
+    num_pages, Hkv, page_size, dk = k_cache.shape
+    if dk != d or block_table.dim() != 2 or block_table.shape[0] != B or tuple(seq_lens.shape) != (B,):
+        raise ValueError("k_cache / block_table / seq_lens shapes disagree with q")
+    _out_check(o, lse, q, torch.bfloat16)
+    nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib().fa_fwd_splitkv_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens),
+                                    _ptr(o), _ptr(lse), B, Hq, Hkv, Nq, d, num_pages, page_size,
+                                    block_table.shape[1], _default_scale(d, scale), int(bool(causal)),
+                                    int(num_splits), _ptr(workspace), nbytes, _stream(stream))
+    _check("fa_fwd_splitkv_paged", st)
+
+
 def fa_combine(o_part, lse_part, o, lse, stream=None):
     """Merge o_part [B,Hq,S,Nq,d] fp32 / lse_part [B,Hq,S,Nq] fp32 into o (bf16) and lse."""
     import torch
@@ -208,4 +239,16 @@ def decode(q, k, v, num_splits, causal=False, scale=None, workspace=None, stream
     if workspace is None:
         workspace = workspace_for(q, num_splits)
     fa_fwd_splitkv(q, k, v, o, lse, num_splits, workspace, scale=scale, causal=causal, stream=stream)
+    return o, lse
+
+
+def decode_paged(q, k_cache, v_cache, block_table, seq_lens, num_splits, causal=False, scale=None, workspace=None,
+                 stream=None):
+    import torch
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = workspace_for(q, num_splits)
+    fa_fwd_splitkv_paged(q, k_cache, v_cache, block_table, seq_lens, o, lse, num_splits, workspace, scale=scale,
+                         causal=causal, stream=stream)
     return o, lse

@@ -129,6 +129,56 @@ fa_status fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, f
   return launched(fa::launch_combine(ca));
 }
 
+fa_status fa_fwd_splitkv_paged(const void* q, const void* k_cache, const void* v_cache, const int* block_table,
+                               const int* seq_lens, void* o, float* lse, int B, int Hq, int Hkv, int Nq, int d,
+                               int num_pages, int page_size, int max_pages, float scale, int causal, int num_splits,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  if (page_size < 16 || page_size > (1 << 16) || (page_size & (page_size - 1)) != 0) return FA_ERR_ARG;
+  if (num_pages < 0 || max_pages < 0) return FA_ERR_SHAPE;
+  if ((long long)max_pages * page_size > 0x7fffffffLL) return FA_ERR_SHAPE;
+  // The caches as [num_pages, Hkv, page_size, d] for the shared checks.
+  fa_status st = check_common(q, k_cache, v_cache, o, lse, B, Hq, Hkv, Nq, 0, d, scale, causal);
+  if (st != FA_OK) return st;
+  if (elems4(num_pages, Hkv, page_size, d) < 0 || elems4(B, max_pages, 1, 1) < 0) return FA_ERR_SHAPE;
+  if (num_splits < 1 || num_splits > kMaxSplits) return FA_ERR_ARG;
+  size_t ob = 0, total = 0;
+  if (!split_ws_sizes(B, Hq, Nq, d, num_splits, &ob, &total)) return FA_ERR_SHAPE;
+  const long long rows = (long long)B * Hq * Nq;
+  if (rows == 0) return FA_OK;
+  if (!seq_lens) return FA_ERR_NULL;
+  if (max_pages > 0) {
+    // Keys may exist: the caches and the table must be there.
+    if (!block_table || !k_cache || !v_cache) return FA_ERR_NULL;
+    if (num_pages < 1) return FA_ERR_SHAPE;
+  }
+  for (const void* p : {(const void*)k_cache, (const void*)v_cache})
+    if (p && !aligned16(p)) return FA_ERR_ALIGN;
+  for (const void* p : {(const void*)block_table, (const void*)seq_lens})
+    if (p && ((uintptr_t)p & 3u) != 0) return FA_ERR_ALIGN;
+  if (!workspace || workspace_bytes < total) return FA_ERR_WORKSPACE;
+  if (((uintptr_t)workspace & 255u) != 0) return FA_ERR_ALIGN;
+  if (fa::splitkv_grid(B, Hq, Hkv, Nq, num_splits) > kMaxGridX || B > kMaxGridYZ || Hkv > kMaxGridYZ)
+    return FA_ERR_UNSUPPORTED;
+  if (fa::combine_grid(B, Hq, Nq) > kMaxGridX) return FA_ERR_UNSUPPORTED;
+  int log2_page = 0;
+  while ((1 << log2_page) < page_size) ++log2_page;
+  float* o_part = (float*)workspace;
+  float* lse_part = (float*)((char*)workspace + ob);
+  fa::FwdArgs f{q, k_cache, v_cache, o, lse, B, Hq, Hkv, Nq, 0, d, scale, causal, stream};
+  fa::SplitArgs sa{f, num_splits, o_part, lse_part};
+  // With max_pages == 0 every sequence is empty and no table entry is read.
+  sa.paged = 1;
+  sa.block_table = block_table;
+  sa.seq_lens = seq_lens;
+  sa.num_pages = num_pages > 0 ? num_pages : 1;
+  sa.log2_page = log2_page;
+  sa.max_pages = max_pages;
+  st = launched(fa::launch_splitkv_partial(sa));
+  if (st != FA_OK) return st;
+  fa::CombineArgs ca{o_part, lse_part, o, lse, B, Hq, Nq, d, num_splits, stream};
+  return launched(fa::launch_combine(ca));
+}
+
 fa_status fa_combine(const float* o_part, const float* lse_part, void* o, float* lse, int B, int Hq, int Nq,
                      int d, int num_splits, void* stream) {
   if (B < 0 || Hq < 1 || Nq < 0) return FA_ERR_SHAPE;

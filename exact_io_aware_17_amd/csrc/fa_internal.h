@@ -23,6 +23,12 @@ struct SplitArgs {
   int num_splits;
   float* o_part;    // [B, Hq, S, Nq, d]
   float* lse_part;  // [B, Hq, S, Nq]
+  // Paged K/V when `paged` is set: f.k, f.v are [num_pages, Hkv,
+  // 2^log2_page, d] caches and f.Nk is unused (per-sequence lengths instead).
+  int paged = 0;
+  const int* block_table = nullptr;  // [B, max_pages]
+  const int* seq_lens = nullptr;     // [B]
+  int num_pages = 0, log2_page = 0, max_pages = 0;
 };
 
 struct CombineArgs {

@@ -23,6 +23,8 @@
 //    O^T += V^T P^T with V^T read transposed from a wave-private LDS slice;
 //  * each wave keeps its own running (m, l, O); the four are merged through
 //    LDS at the end and the chunk's normalised O_s and LSE_s are written.
+#include <type_traits>
+
 #include "fa_common.h"
 #include "fa_internal.h"
 
@@ -45,16 +47,42 @@ struct SplitStage {
 // consecutive keys, the key-contiguous B operand of the P.V MFMA.
 __device__ __forceinline__ int blk_key(int i16, int sb) { return 8 * (i16 >> 2) + 4 * sb + (i16 & 3); }
 
+// Where the key rows of one KV head live.
+//  Contiguous: rows key * D of [Nk, D] tensors.
+//  Paged: the cache is [num_pages, Hkv, page, D]; logical page j of the
+//  sequence is physical page block_table[j]. Pages hold at least 16 keys, so
+//  the 32 keys of a block (which starts wherever its chunk does) span at most
+//  three pages; `pg` holds the physical pages of logical pages
+//  kb / page .. kb / page + 2.
 template <int D>
-__device__ __forceinline__ void load_stage(SplitStage<D>& st, const uint16_t* __restrict__ Kh,
-                                           const uint16_t* __restrict__ Vh, int kb, int k1, int lane) {
+struct ContigRows {
+  const uint16_t* k;
+  const uint16_t* v;
+  __device__ __forceinline__ size_t row(int key, int /*kb*/, const int (&/*pg*/)[3]) const { return (size_t)key * D; }
+};
+template <int D>
+struct PagedRows {
+  const uint16_t* k;  // cache base + head offset (g * page * D)
+  const uint16_t* v;
+  int log2_page;
+  int head_stride;    // Hkv * page * D
+  __device__ __forceinline__ size_t row(int key, int kb, const int (&pg)[3]) const {
+    const int sub = (key >> log2_page) - (kb >> log2_page);
+    const int page = sub == 0 ? pg[0] : (sub == 1 ? pg[1] : pg[2]);
+    return (size_t)page * head_stride + (size_t)(key & ((1 << log2_page) - 1)) * D;
+  }
+};
+
+template <int D, typename Rows>
+__device__ __forceinline__ void load_stage(SplitStage<D>& st, const Rows& src, int kb, int k1, const int (&pg)[3],
+                                           int lane) {
   constexpr int KS = D / 32;
   const int i16 = lane & 15, g4 = lane >> 4;
 #pragma unroll
   for (int sb = 0; sb < 2; ++sb) {
     int key = kb + blk_key(i16, sb);
     key = key < k1 ? key : k1 - 1;
-    const uint16_t* row = Kh + (size_t)key * D + 8 * g4;
+    const uint16_t* row = src.k + src.row(key, kb, pg) + 8 * g4;
 #pragma unroll
     for (int s = 0; s < KS; ++s) st.k[sb][s] = *reinterpret_cast<const bf16x8*>(row + 32 * s);
   }
@@ -63,15 +91,20 @@ __device__ __forceinline__ void load_stage(SplitStage<D>& st, const uint16_t* __
   for (int t = 0; t < kBlk * D / 8 / 64; ++t) {
     int key = kb + t * RPI + lane / CH;
     key = key < k1 ? key : k1 - 1;
-    st.v[t] = *reinterpret_cast<const u32x4*>(Vh + (size_t)key * D + (lane % CH) * 8);
+    st.v[t] = *reinterpret_cast<const u32x4*>(src.v + src.row(key, kb, pg) + (lane % CH) * 8);
   }
 }
 
-template <int D>
+// PAGED: K and V are page caches [num_pages, Hkv, 2^log2_page, D], each
+// sequence's pages listed in block_table [B, max_pages] and its key count in
+// seq_lens [B]; the chunk size is then per sequence. Table entries and lengths
+// out of range are clamped into range (memory stays in bounds).
+template <int D, bool PAGED>
 __global__ __launch_bounds__(kSplitThreads, 2) void splitkv_partial_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     float* __restrict__ Opart, float* __restrict__ LSEpart, int Hq, int Hkv, int Nq, int Nk,
-    float sl2, int causal, int S, int chunk) {
+    float sl2, int causal, int S, int chunk, const int* __restrict__ block_table,
+    const int* __restrict__ seq_lens, int num_pages, int log2_page, int max_pages) {
   constexpr int KS = D / 32;    // k-steps of the score MFMA
   constexpr int DB = D / 16;    // 16-wide d blocks of O
   constexpr int CH = D / 8, RPI = 64 / CH, VI = kBlk * D / 8 / 64;
@@ -88,6 +121,13 @@ __global__ __launch_bounds__(kSplitThreads, 2) void splitkv_partial_kernel(
   const bool rvalid = r < R;
   const int hh = rvalid ? r / Nq : 0, qi = rvalid ? r - hh * Nq : 0;
   const int head = g * G + hh;
+  const int* bt = block_table + (size_t)b * max_pages;
+  if constexpr (PAGED) {
+    const long cap = (long)max_pages << log2_page;
+    const long n = seq_lens[b];
+    Nk = n < 0 ? 0 : (int)(n < cap ? n : cap);
+    chunk = (int)(((long)Nk + S - 1) / S);
+  }
   const int diag = Nk - Nq;
 
   bf16x8 qf[KS];
@@ -104,8 +144,28 @@ __global__ __launch_bounds__(kSplitThreads, 2) void splitkv_partial_kernel(
   const int nbw = nblk > wave ? (nblk - wave + 3) / 4 : 0;  // blocks of this wave
   const int lim = causal ? qi + diag : 0x7fffffff;
 
-  const uint16_t* Kh = K + (size_t)(b * Hkv + g) * Nk * D;
-  const uint16_t* Vh = V + (size_t)(b * Hkv + g) * Nk * D;
+  using Rows = typename std::conditional<PAGED, PagedRows<D>, ContigRows<D>>::type;
+  Rows src;
+  if constexpr (PAGED) {
+    const size_t head_off = (size_t)g << log2_page;
+    src = Rows{K + head_off * D, V + head_off * D, log2_page, (Hkv << log2_page) * D};
+  } else {
+    src = Rows{K + (size_t)(b * Hkv + g) * Nk * D, V + (size_t)(b * Hkv + g) * Nk * D};
+  }
+  // Physical pages of the block starting at key kb (unused when contiguous).
+  auto pages_of = [&](int kb, int (&pg)[3]) __attribute__((always_inline)) {
+    if constexpr (PAGED) {
+      const int lp = kb >> log2_page;
+#pragma unroll
+      for (int j = 0; j < 3; ++j) {
+        const int l = lp + j < max_pages ? lp + j : max_pages - 1;
+        const int p = bt[l];
+        pg[j] = p < 0 ? 0 : (p < num_pages ? p : num_pages - 1);
+      }
+    } else {
+      pg[0] = pg[1] = pg[2] = 0;
+    }
+  };
   uint16_t* vw = vlds[wave];
   const char* vw_c = reinterpret_cast<const char*>(vw);
 
@@ -136,8 +196,17 @@ __global__ __launch_bounds__(kSplitThreads, 2) void splitkv_partial_kernel(
   float m_run = kNegInf, l_run = 0.f;
 
   SplitStage<D> st[2];
-  if (nbw > 0) load_stage<D>(st[0], Kh, Vh, k0 + kBlk * wave, k1, lane);
-  if (nbw > 1) load_stage<D>(st[1], Kh, Vh, k0 + kBlk * (wave + 4), k1, lane);
+  // Page numbers are fetched one block ahead of the loads that use them.
+  int pg_cur[3], pg_next[3];
+  if (nbw > 0) {
+    pages_of(k0 + kBlk * wave, pg_cur);
+    load_stage<D>(st[0], src, k0 + kBlk * wave, k1, pg_cur, lane);
+  }
+  if (nbw > 1) {
+    pages_of(k0 + kBlk * (wave + 4), pg_cur);
+    load_stage<D>(st[1], src, k0 + kBlk * (wave + 4), k1, pg_cur, lane);
+  }
+  if (nbw > 2) pages_of(k0 + kBlk * (wave + 8), pg_next);
 
   auto block = [&](SplitStage<D>& cur, int i) {
     const int kb = k0 + kBlk * (wave + 4 * i);
@@ -149,7 +218,11 @@ __global__ __launch_bounds__(kSplitThreads, 2) void splitkv_partial_kernel(
       sc[0] = mfma16(cur.k[0][k], qf[k], sc[0]);
       sc[1] = mfma16(cur.k[1][k], qf[k], sc[1]);
     }
-    if (i + 2 < nbw) load_stage<D>(cur, Kh, Vh, k0 + kBlk * (wave + 4 * (i + 2)), k1, lane);
+    if (i + 2 < nbw) {
+      const int nb[3] = {pg_next[0], pg_next[1], pg_next[2]};
+      if (i + 3 < nbw) pages_of(k0 + kBlk * (wave + 4 * (i + 3)), pg_next);
+      load_stage<D>(cur, src, k0 + kBlk * (wave + 4 * (i + 2)), k1, nb, lane);
+    }
     if (kb + kBlk > k1 || causal) {
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb)
@@ -315,10 +388,11 @@ hipError_t launch_partial_d(const SplitArgs& a) {
   const int S = a.num_splits;
   const int chunk = (int)(((long)f.Nk + S - 1) / S);
   const float sl2 = f.scale * kLog2e;
-  hipLaunchKernelGGL(splitkv_partial_kernel<D>, dim3((unsigned)(S * nrb), (unsigned)f.Hkv, (unsigned)f.B),
-                     dim3(kSplitThreads), 0, (hipStream_t)f.stream, (const uint16_t*)f.q, (const uint16_t*)f.k,
-                     (const uint16_t*)f.v, a.o_part, a.lse_part, f.Hq, f.Hkv, f.Nq, f.Nk, sl2, f.causal, S,
-                     chunk);
+  auto* kernel = a.paged ? splitkv_partial_kernel<D, true> : splitkv_partial_kernel<D, false>;
+  hipLaunchKernelGGL(kernel, dim3((unsigned)(S * nrb), (unsigned)f.Hkv, (unsigned)f.B), dim3(kSplitThreads), 0,
+                     (hipStream_t)f.stream, (const uint16_t*)f.q, (const uint16_t*)f.k, (const uint16_t*)f.v,
+                     a.o_part, a.lse_part, f.Hq, f.Hkv, f.Nq, f.Nk, sl2, f.causal, S, chunk, a.block_table,
+                     a.seq_lens, a.num_pages, a.log2_page, a.max_pages);
   return hipGetLastError();
 }
 

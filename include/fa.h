@@ -107,6 +107,35 @@ fa_status fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, f
                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * fa_fwd_splitkv_paged -- fa_fwd_splitkv over a paged K/V cache, one key
+ * count per sequence.  PagedAttention appears on the "flash attention v3
+ * paper" search-result page only as a name; the cache layout, table and
+ * length conventions below are this library's.
+ *   k_cache, v_cache : [num_pages, Hkv, page_size, d] bf16 (each page holds
+ *                      page_size consecutive keys of one KV head);
+ *   block_table      : int32 [B, max_pages]; logical page j of sequence b
+ *                      (keys j*page_size .. (j+1)*page_size-1) is physical
+ *                      page block_table[b*max_pages + j];
+ *   seq_lens         : int32 [B], the number of keys of each sequence
+ *                      (0 <= seq_lens[b] <= max_pages * page_size);
+ *   q, o, lse        : as fa_fwd_splitkv ([B,Hq,Nq,d], [B,Hq,Nq]).
+ * Sequence b is attended as fa_fwd_splitkv attends Nk = seq_lens[b] keys
+ * (causal: key j visible to query i iff j <= i + seq_lens[b] - Nq), cut into
+ * num_splits chunks of ceil(seq_lens[b] / num_splits) keys, then merged.
+ * page_size must be a power of two in [16, 65536].  Table entries outside
+ * [0, num_pages) and lengths outside [0, max_pages*page_size] are clamped into
+ * range on the device (memory stays in bounds; such results are unspecified).
+ * block_table and seq_lens are device pointers, 4-byte aligned; the
+ * workspace is the same as fa_fwd_splitkv's (fa_splitkv_workspace_bytes).
+ */
+fa_status fa_fwd_splitkv_paged(const void* q, const void* k_cache, const void* v_cache,
+                               const int* block_table, const int* seq_lens, void* o, float* lse,
+                               int B, int Hq, int Hkv, int Nq, int d,
+                               int num_pages, int page_size, int max_pages,
+                               float scale, int causal, int num_splits,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * fa_combine -- LSE-weighted merge of per-chunk results.
  * o_part [B,Hq,S,Nq,d] fp32, lse_part [B,Hq,S,Nq] fp32 in; o [B,Hq,Nq,d] bf16
  * and lse [B,Hq,Nq] fp32 out.  With M = max_s LSE_s, w_s = exp(LSE_s - M):

@@ -14,11 +14,18 @@ Parity status of each function (the pins live in tests/test_oracle.py):
 * ``split_bounds``, ``splitkv_partials``, ``combine`` -- pinned (combine of the
                            partials equals unsplit attention; one split is the
                            identity; empty chunks get weight zero).
+* ``paged_gather``, ``paged_attention`` -- pinned (a cache built from contiguous
+                           K/V under any page permutation gives back those K/V
+                           and their attention; truncated lengths equal
+                           attention over the first keys; brute force on a
+                           tiny case).
 """
 from .attention import (  # noqa: F401
     attention,
     attention_online,
     combine,
+    paged_attention,
+    paged_gather,
     split_bounds,
     splitkv_partials,
 )

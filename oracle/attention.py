@@ -32,6 +32,11 @@ Readings where the pages are silent (each also listed in the design notes):
   key gets the same partial result and weight zero in the combine.
 * Split chunks are contiguous along keys: chunk s covers
   [s*C, min(Nk, (s+1)*C)) with C = ceil(Nk / num_splits).
+* Paged K/V (PagedAttention is only named on the "flash attention v3 paper"
+  search-result page): a cache [num_pages, Hkv, page, d] whose page p holds
+  `page` consecutive keys of each KV head, a table [B, max_pages] naming the
+  physical page of each logical page of a sequence, and one key count per
+  sequence. Paged attention is plain attention over the gathered keys.
 """
 from __future__ import annotations
 
@@ -216,3 +221,31 @@ def combine(o_part, lse_part):
     lse[alive] = m[alive] + np.log(den[alive])
     return o, lse
 
+
+
+def paged_gather(k_cache, v_cache, block_table, seq_len, b):
+    """Keys 0 .. seq_len-1 of sequence b, gathered page by page from the
+    caches [num_pages, Hkv, page, d]: logical page j is physical page
+    block_table[b, j].  Returns (k [Hkv, seq_len, d], v [Hkv, seq_len, d])."""
+    num_pages, Hkv, page, d = k_cache.shape
+    n_pages = -(-seq_len // page)
+    pages = np.asarray(block_table[b, :n_pages], dtype=np.int64)
+    k = np.concatenate([k_cache[p] for p in pages], axis=1) if n_pages else np.zeros((Hkv, 0, d))
+    v = np.concatenate([v_cache[p] for p in pages], axis=1) if n_pages else np.zeros((Hkv, 0, d))
+    return k[:, :seq_len], v[:, :seq_len]
+
+
+def paged_attention(q, k_cache, v_cache, block_table, seq_lens, scale, causal=False):
+    """Attention of sequence b over its own seq_lens[b] keys, gathered from the
+    page caches; each sequence is the plain definition with Nk = seq_lens[b]
+    (so the causal diagonal sits at seq_lens[b] - Nq).
+    q [B, Hq, Nq, d]; returns (O [B, Hq, Nq, d], LSE [B, Hq, Nq])."""
+    q = np.asarray(q, dtype=np.float64)
+    B, Hq, Nq, d = q.shape
+    o = np.zeros((B, Hq, Nq, d))
+    lse = np.full((B, Hq, Nq), NEG_INF)
+    for b in range(B):
+        k, v = paged_gather(k_cache, v_cache, block_table, int(seq_lens[b]), b)
+        ob, lb = attention(q[b:b + 1], k[None], v[None], scale, causal)
+        o[b], lse[b] = ob[0], lb[0]
+    return o, lse

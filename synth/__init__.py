@@ -178,3 +178,13 @@ def inputs_f64(w: Workload, bf16: bool = True, q_heads=None, kv_heads=None, q_ro
     k = get(TENSOR_K, w.kv_shape, kv_heads)
     v = get(TENSOR_V, w.kv_shape, kv_heads)
     return q, k, v
+
+
+def page_table(B: int, max_pages: int, seed: int, spare: int = 0):
+    """A paged K/V layout: the physical page of each (sequence, logical page),
+    a seeded random permutation of B * max_pages + spare pages (the spare ones
+    stay unused).  Returns (num_pages, table int32 [B, max_pages])."""
+    r = np.random.default_rng([seed, 0x9A6E])
+    num_pages = B * max_pages + spare
+    perm = r.permutation(num_pages).astype(np.int32)
+    return num_pages, perm[: B * max_pages].reshape(B, max_pages)

@@ -80,3 +80,42 @@ def sample_rows(nq, n_random=24, seed=0, tile=128):
     rows = set(x for x in edges if 0 <= x < nq)
     rows.update(r.integers(0, nq, size=min(n_random, nq)).tolist())
     return np.array(sorted(rows))
+
+
+def _pages(x, page, mp):
+    """[B, Hkv, Nk, d] -> [B * mp, Hkv, page, d], logical page j of sequence b at row b * mp + j."""
+    B, Hkv, Nk, d = x.shape
+    return x.reshape(B, Hkv, mp, page, d).transpose(0, 2, 1, 3, 4).reshape(B * mp, Hkv, page, d)
+
+
+def paged_numpy(k, v, page, seed, spare=5, filler=3.0):
+    """Page caches [num_pages, Hkv, page, d] holding K/V [B, Hkv, Nk, d] under
+    synth.page_table's permutation; unused slots hold `filler`."""
+    B, Hkv, Nk, d = k.shape
+    mp = -(-Nk // page)
+    num_pages, table = synth.page_table(B, mp, seed, spare)
+    pad = ((0, 0), (0, 0), (0, mp * page - Nk), (0, 0))
+    out = []
+    for x in (k, v):
+        cache = np.full((num_pages, Hkv, page, d), filler, dtype=x.dtype)
+        cache[table.reshape(-1)] = _pages(np.pad(x, pad), page, mp)
+        out.append(cache)
+    return out[0], out[1], table
+
+
+def paged_device(k, v, page, seed, spare=5, filler=3.0):
+    """The same layout built on the GPU from device K/V tensors."""
+    import torch
+    B, Hkv, Nk, d = k.shape
+    mp = -(-Nk // page)
+    num_pages, table = synth.page_table(B, mp, seed, spare)
+    idx = torch.from_numpy(table.reshape(-1).astype(np.int64)).to(k.device)
+    out = []
+    for x in (k, v):
+        if mp * page != Nk:
+            x = torch.nn.functional.pad(x, (0, 0, 0, mp * page - Nk))
+        pages = x.reshape(B, Hkv, mp, page, d).permute(0, 2, 1, 3, 4).reshape(B * mp, Hkv, page, d)
+        cache = torch.full((num_pages, Hkv, page, d), filler, dtype=x.dtype, device=x.device)
+        cache[idx] = pages
+        out.append(cache.contiguous())
+    return out[0], out[1], torch.from_numpy(table).to(k.device)

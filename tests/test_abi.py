@@ -28,8 +28,8 @@ def _declarations():
 
 def test_header_declarations_found():
     d = _declarations()
-    assert set(d) == {"fa_fwd", "fa_fwd_fp32", "fa_splitkv_workspace_bytes", "fa_fwd_splitkv", "fa_combine",
-                      "fa_status_str"}
+    assert set(d) == {"fa_fwd", "fa_fwd_fp32", "fa_splitkv_workspace_bytes", "fa_fwd_splitkv",
+                      "fa_fwd_splitkv_paged", "fa_combine", "fa_status_str"}
 
 
 def test_library_exports_every_declared_symbol():
@@ -109,6 +109,40 @@ def test_splitkv_argument_checks():
     assert _split(d=80) == 3
     assert _split(scale=-1.0) == 7
     assert _split(B=70000) == 3  # grid z limit
+
+
+def _paged(q=P, kc=P, vc=P, bt=P, sl=P, o=P, lse=P, B=2, Hq=8, Hkv=2, Nq=1, d=128, num_pages=64, page=16,
+           max_pages=8, scale=0.1, causal=0, S=4, ws=0x100000, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = fa.fa_splitkv_workspace_bytes(B, Hq, Nq, d, S)
+    return fa.lib().fa_fwd_splitkv_paged(q, kc, vc, bt, sl, o, lse, B, Hq, Hkv, Nq, d, num_pages, page, max_pages,
+                                         scale, causal, S, ws, ws_bytes, None)
+
+
+def test_paged_argument_checks():
+    for page in (0, 8, 24, 1 << 17, -16):
+        assert _paged(page=page) == 7, page
+    assert _paged(num_pages=-1) == 2
+    assert _paged(max_pages=-1) == 2
+    assert _paged(max_pages=1 << 28, page=1 << 10) == 2
+    assert _paged(q=None) == 1
+    assert _paged(o=P + 4) == 4
+    assert _paged(d=96) == 3
+    assert _paged(Hq=7) == 2
+    assert _paged(scale=0.0) == 7
+    assert _paged(causal=3) == 7
+    assert _paged(S=0) == 7
+    assert _paged(sl=None) == 1
+    assert _paged(bt=None) == 1
+    assert _paged(kc=None) == 1
+    assert _paged(num_pages=0) == 2
+    assert _paged(kc=P + 8) == 4
+    assert _paged(bt=P + 2) == 4
+    assert _paged(sl=P + 1) == 4
+    assert _paged(ws=None) == 5
+    assert _paged(ws_bytes=64) == 5
+    assert _paged(ws=0x100000 + 64) == 4
+    assert _paged(B=70000) == 3
 
 
 def test_combine_argument_checks():

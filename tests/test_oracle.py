@@ -178,3 +178,75 @@ def test_generic_unmutated_passes():
     """The harness used for the mutants is itself correct when unmutated."""
     for pin in P.ALL_PINS:
         pin(_generic)
+
+
+# --- paged K/V -------------------------------------------------------------
+
+def _paged_cache(k, v, page, seed, spare=3):
+    """A page cache [num_pages, Hkv, page, d] holding contiguous K/V
+    [B, Hkv, Nk, d] under a random page permutation (plus unused pages full of
+    noise), and its block table [B, max_pages]."""
+    r = np.random.default_rng(seed)
+    B, Hkv, Nk, d = k.shape
+    max_pages = -(-Nk // page)
+    num_pages = B * max_pages + spare
+    perm = r.permutation(num_pages)
+    kc = r.standard_normal((num_pages, Hkv, page, d))
+    vc = r.standard_normal((num_pages, Hkv, page, d))
+    table = np.zeros((B, max_pages), dtype=np.int32)
+    for b in range(B):
+        for j in range(max_pages):
+            p = perm[b * max_pages + j]
+            table[b, j] = p
+            n = min(page, Nk - j * page)
+            kc[p, :, :n] = k[b, :, j * page: j * page + n]
+            vc[p, :, :n] = v[b, :, j * page: j * page + n]
+    return kc, vc, table
+
+
+@pytest.mark.parametrize("page", [1, 4, 16])
+def test_paged_gather_gives_back_the_keys(page):
+    r = np.random.default_rng(11)
+    k = r.standard_normal((3, 2, 37, 4))
+    v = r.standard_normal((3, 2, 37, 4))
+    kc, vc, table = _paged_cache(k, v, page, seed=page)
+    for b, L in ((0, 37), (1, 20), (2, 0), (2, 1)):
+        kg, vg = oracle.paged_gather(kc, vc, table, L, b)
+        assert kg.shape == (2, L, 4) and vg.shape == (2, L, 4)
+        assert np.array_equal(kg, k[b, :, :L]) and np.array_equal(vg, v[b, :, :L])
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_paged_attention_is_attention_over_each_sequence(causal):
+    r = np.random.default_rng(12)
+    B, Hq, Hkv, Nq, Nk, d = 3, 4, 2, 3, 50, 8
+    q = r.standard_normal((B, Hq, Nq, d))
+    k = r.standard_normal((B, Hkv, Nk, d))
+    v = r.standard_normal((B, Hkv, Nk, d))
+    kc, vc, table = _paged_cache(k, v, 16, seed=3)
+    lens = np.array([50, 17, 2], dtype=np.int32)
+    o, lse = oracle.paged_attention(q, kc, vc, table, lens, 0.3, causal)
+    for b in range(B):
+        L = int(lens[b])
+        ob, lb = oracle.attention(q[b:b + 1], k[b:b + 1, :, :L], v[b:b + 1, :, :L], 0.3, causal)
+        assert np.allclose(o[b], ob[0], rtol=0, atol=1e-13) and np.allclose(lse[b], lb[0], rtol=0, atol=1e-13)
+    # rows whose causal window holds no key: O = 0, LSE = -inf
+    if causal:
+        assert np.all(np.isneginf(lse[2, :, 0])) and np.all(o[2, :, 0] == 0)
+
+
+def test_paged_attention_brute_force():
+    """A tiny paged case against pure-Python loops on the gathered keys."""
+    r = np.random.default_rng(13)
+    k = r.standard_normal((2, 1, 5, 3))
+    v = r.standard_normal((2, 1, 5, 3))
+    q = r.standard_normal((2, 2, 2, 3))
+    kc, vc, table = _paged_cache(k, v, 2, seed=4)
+    lens = np.array([5, 3], dtype=np.int32)
+    for causal in (False, True):
+        o, lse = oracle.paged_attention(q, kc, vc, table, lens, 0.7, causal)
+        for b in range(2):
+            L = int(lens[b])
+            ob, lb = P.brute_attention(q[b:b + 1], k[b:b + 1, :, :L], v[b:b + 1, :, :L], 0.7, causal)
+            assert np.allclose(o[b], ob[0], rtol=0, atol=1e-12)
+            assert np.allclose(lse[b], lb[0], rtol=0, atol=1e-12)

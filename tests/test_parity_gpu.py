@@ -7,7 +7,7 @@ import pytest
 import oracle
 import synth
 from gpu_helpers import (F32_TOL, assert_close, device_inputs, errors, oracle_full, oracle_sample,
-                         sample_rows, say)
+                         paged_device, paged_numpy, sample_rows, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -153,6 +153,83 @@ def test_decode_edge_cases(w):
     assert_close(errors(o, o_ref, lse, l_ref), what=w.name)
     op_ref, lp_ref = oracle.splitkv_partials(q, k, v, w.scale, w.num_splits, w.causal)
     assert_close(errors(op, op_ref, lp, lp_ref), what=w.name + " partials")
+
+
+# Paged K/V: (workload for the shapes, per-sequence key counts, page size).
+PAGED = [
+    (synth.Workload("paged16_gqa", 3, 8, 2, 1, 1000, 128, num_splits=4), [1000, 1, 517], 16),
+    (synth.Workload("paged64_multiquery_causal", 3, 6, 2, 3, 300, 128, causal=True, num_splits=3, seed=8),
+     [300, 64, 129], 64),
+    (synth.Workload("paged32_d64_empty_sequence", 3, 4, 4, 1, 200, 64, num_splits=7, seed=9), [200, 0, 33], 32),
+    (synth.Workload("paged256_causal_two_chunks", 2, 4, 1, 2, 700, 128, causal=True, num_splits=2, seed=10),
+     [700, 256], 256),
+]
+
+
+@pytest.mark.parametrize("case", PAGED, ids=lambda c: c[0].name)
+def test_paged_decode(case):
+    """fa_fwd_splitkv_paged on a randomly permuted page cache against the
+    paged oracle (each sequence its own key count)."""
+    import torch
+    fa = _fa()
+    w, lens, page = case
+    q, k, v = device_inputs(w)
+    kc, vc, table = paged_device(k, v, page, seed=w.seed + page)
+    sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    say(f"case paged decode {w.name} page={page} lens={lens}")
+    o, lse = fa.decode_paged(q, kc, vc, table, sl, w.num_splits, causal=w.causal, scale=w.scale)
+    torch.cuda.synchronize()
+    q64, k64, v64 = synth.inputs_f64(w)
+    kc64, vc64, table64 = paged_numpy(k64, v64, page, seed=w.seed + page)
+    assert np.array_equal(table64, table.cpu().numpy())
+    o_ref, l_ref = oracle.paged_attention(q64, kc64, vc64, table64, lens, w.scale, w.causal)
+    o_got = o.float().cpu().numpy().astype(np.float64)
+    l_got = lse.cpu().numpy().astype(np.float64)
+    assert_close(errors(o_got, o_ref, l_got, l_ref), what=w.name)
+    for b, L in enumerate(lens):
+        if L == 0:
+            assert np.all(o_got[b] == 0) and np.all(np.isneginf(l_got[b]))
+
+
+def test_paged_identity_layout_matches_contiguous():
+    """Pages laid out in order (page j of sequence b at b * pages + j) give
+    bit-identical results to the contiguous split-KV path."""
+    import torch
+    fa = _fa()
+    w = synth.Workload("paged_identity", 2, 8, 2, 1, 1024, 128, num_splits=5, seed=12)
+    q, k, v = device_inputs(w)
+    page, mp = 16, 1024 // 16
+    kc = k.reshape(2, 2, mp, page, 128).permute(0, 2, 1, 3, 4).reshape(2 * mp, 2, page, 128).contiguous()
+    vc = v.reshape(2, 2, mp, page, 128).permute(0, 2, 1, 3, 4).reshape(2 * mp, 2, page, 128).contiguous()
+    table = torch.arange(2 * mp, dtype=torch.int32, device="cuda").reshape(2, mp)
+    sl = torch.full((2,), 1024, dtype=torch.int32, device="cuda")
+    say("case paged identity layout")
+    o1, l1 = fa.decode_paged(q, kc, vc, table, sl, w.num_splits, scale=w.scale)
+    o2, l2 = fa.decode(q, k, v, w.num_splits, scale=w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_paged_decode_full_size():
+    """The benchmark's paged decode (GQA decode workload, 16-key pages in a
+    random order); oracle on every row of three batches."""
+    import torch
+    fa = _fa()
+    w = W["gqa_decode_b64_hq32_hkv8_kv8192"]
+    q, k, v = device_inputs(w)
+    kc, vc, table = paged_device(k, v, 16, seed=w.seed + 16)
+    del k, v
+    sl = torch.full((w.B,), w.Nk, dtype=torch.int32, device="cuda")
+    say("case paged decode full-size")
+    o, lse = fa.decode_paged(q, kc, vc, table, sl, w.num_splits, scale=w.scale)
+    torch.cuda.synchronize()
+    o = o.float().cpu().numpy().astype(np.float64)
+    lse = lse.cpu().numpy().astype(np.float64)
+    for b in (0, 31, 63):
+        q64, k64, v64 = synth.inputs_f64(w, q_heads=[(b, h) for h in range(w.Hq)],
+                                         kv_heads=[(b, g) for g in range(w.Hkv)])
+        o_ref, l_ref = oracle.attention(q64[None], k64[None], v64[None], w.scale, False)
+        assert_close(errors(o[b], o_ref[0], lse[b], l_ref[0]), what=f"paged decode b={b}")
 
 
 @pytest.mark.parametrize("S,d", [(5, 128), (64, 128), (100, 128), (7, 64), (70, 64)])
