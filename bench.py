@@ -4,10 +4,11 @@ Default run (N=1): the pages' benchmark shape (B=1, H=8, Nq=4096, Nk=8192,
 d=128, bf16, non-causal) through fa_fwd, W warm-up steps then exactly K timed
 steps; one JSON line on stdout. The line also carries the split-KV decode
 workload (B=64, Hq=32, Hkv=8, Nk=8192, 16 splits) timed the same way, the
+same decode over a paged K/V cache (16-key pages in a random order), the
 roofline of the dominant kernel, and the CPU oracle timed on a bounded sample.
 
   python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--all]
-  python bench.py --only prefill|decode --steps 3   (short runs under a profiler)
+  python bench.py --only prefill|decode|decode_paged --steps 3   (short runs under a profiler)
   python bench.py --copy-calib                       (plain copy of known size, for counter scaling)
 """
 from __future__ import annotations
@@ -138,6 +139,53 @@ def bench_decode(w, steps, warmup, device, min_warm_s=0.2):
             "gbs": nbytes / (wall / steps) / 1e9, "kernel_gbs": nbytes / (ev_ms * 1e-3) / 1e9}
 
 
+PAGE = 16  # keys per page of the paged decode benchmark
+
+
+def paged_caches(k, v, page, seed):
+    """K/V [B, Hkv, Nk, d] laid out as page caches [num_pages, Hkv, page, d]
+    in the seeded random page order of synth.page_table; returns
+    (k_cache, v_cache, block_table int32 [B, max_pages])."""
+    import torch
+    B, Hkv, Nk, d = k.shape
+    mp = -(-Nk // page)
+    num_pages, table = synth.page_table(B, mp, seed)
+    idx = torch.from_numpy(table.reshape(-1).astype("int64")).to(k.device)
+    out = []
+    for x in (k, v):
+        if mp * page != Nk:
+            x = torch.nn.functional.pad(x, (0, 0, 0, mp * page - Nk))
+        pages = x.reshape(B, Hkv, mp, page, d).permute(0, 2, 1, 3, 4).reshape(B * mp, Hkv, page, d)
+        cache = torch.empty((num_pages, Hkv, page, d), dtype=x.dtype, device=x.device)
+        cache[idx] = pages
+        out.append(cache)
+    return out[0], out[1], torch.from_numpy(table).to(k.device)
+
+
+def bench_decode_paged(w, steps, warmup, device, page=PAGE, min_warm_s=0.2):
+    """The decode workload over paged K/V (16-key pages in a random order);
+    three caches rotate so that no step reads cache-warm data."""
+    import torch
+    import exact_io_aware_17_amd as fa
+    q, k, v = device_inputs(w, device)
+    caches = [paged_caches(k, v, page, seed=w.seed + i) for i in range(3)]
+    del k, v
+    sl = torch.full((w.B,), w.Nk, dtype=torch.int32, device=device)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=device)
+    ws = fa.workspace_for(q, w.num_splits)
+    it = [0]
+
+    def step():
+        kc, vc, table = caches[it[0] % len(caches)]
+        it[0] += 1
+        fa.fa_fwd_splitkv_paged(q, kc, vc, table, sl, o, lse, w.num_splits, ws, scale=w.scale)
+    wall, ev_ms = time_steps(step, steps, warmup, min_warm_s)
+    nbytes = w.algorithmic_bytes() + caches[0][2].numel() * 4 + w.B * 4  # + block table and lengths
+    return {"wall_s": wall, "ms_per_step": wall * 1e3 / steps, "kernel_ms": ev_ms, "page": page,
+            "gbs": nbytes / (wall / steps) / 1e9, "kernel_gbs": nbytes / (ev_ms * 1e-3) / 1e9}
+
+
 def cpu_baseline(w, budget_s=15.0):
     """The fp64 oracle on the host, head by head, until the budget is spent."""
     import oracle
@@ -185,7 +233,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--all", action="store_true", help="also time the other prefill workloads")
-    ap.add_argument("--only", choices=["prefill", "decode"], default=None)
+    ap.add_argument("--only", choices=["prefill", "decode", "decode_paged"], default=None)
     ap.add_argument("--copy-calib", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -214,6 +262,10 @@ def main():
         r = bench_decode(wd, args.steps, args.warmup, device, min_warm_s=0.0)
         print(json.dumps({"only": "decode", **r}))
         return
+    if args.only == "decode_paged":
+        r = bench_decode_paged(wd, args.steps, args.warmup, device, min_warm_s=0.0)
+        print(json.dumps({"only": "decode_paged", **r}))
+        return
 
     log(f"prefill {wp.name}: warmup {args.warmup}, steps {args.steps}")
     rp = bench_prefill(wp, args.steps, args.warmup, device)
@@ -221,6 +273,9 @@ def main():
     log(f"decode {wd.name}: warmup {args.warmup}, steps {args.steps}")
     rd = bench_decode(wd, args.steps, args.warmup, device)
     log(f"  {rd}")
+    log(f"paged decode {wd.name}, {PAGE}-key pages: warmup {args.warmup}, steps {args.steps}")
+    rdp = bench_decode_paged(wd, args.steps, args.warmup, device)
+    log(f"  {rdp}")
     others = {}
     if args.all:
         for name in OTHER_PREFILL:
@@ -234,6 +289,7 @@ def main():
 
     fwd_traffic = traffic_from_profile("fwd_bf16_pages_shape_traffic.md", FWD_SOURCES)
     dec_traffic = traffic_from_profile("splitkv_decode_traffic.md", DEC_SOURCES)
+    decp_traffic = traffic_from_profile("splitkv_paged_decode_traffic.md", DEC_SOURCES)
     line = {
         "metric": "attention fwd TFLOPS (4*B*H*Nq*Nk*d per forward) on the pages' shape; decode HBM GB/s",
         "value": round(rp["tflops"], 2),
@@ -258,7 +314,15 @@ def main():
                    "roofline": {"bound": "hbm", "achieved": round(rd["kernel_gbs"], 1), "peak": PEAK_HBM_GBS,
                                 "unit": "GB/s", "frac": round(rd["kernel_gbs"] / PEAK_HBM_GBS, 4),
                                 "traffic": dec_traffic, "kernel_ms": round(rd["kernel_ms"], 5),
-                                "kernel": "splitkv_partial_kernel<128> + combine_kernel<128>"}},
+                                "kernel": "splitkv_partial_kernel<128, false> + combine_kernel<128>"}},
+        "decode_paged": {"workload": f"{wd.name}_paged{PAGE}", "page_size": PAGE,
+                         "metric": "paged decode HBM GB/s (algorithmic bytes incl. block table / step time)",
+                         "value": round(rdp["gbs"], 1), "unit": "GB/s", "ms_per_step": round(rdp["ms_per_step"], 5),
+                         "roofline": {"bound": "hbm", "achieved": round(rdp["kernel_gbs"], 1),
+                                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                      "frac": round(rdp["kernel_gbs"] / PEAK_HBM_GBS, 4), "traffic": decp_traffic,
+                                      "kernel_ms": round(rdp["kernel_ms"], 5),
+                                      "kernel": "splitkv_partial_kernel<128, true> + combine_kernel<128>"}},
     }
     if others:
         line["other_prefill"] = others
