@@ -19,6 +19,16 @@ Parity status of each function (the pins live in tests/test_oracle.py):
                            and their attention; truncated lengths equal
                            attention over the first keys; brute force on a
                            tiny case).
+* ``e4m3_decode``, ``e4m3_value`` -- pinned (closed-form codes of the OCP E4M3
+                           format; every code against torch's float8_e4m3fn
+                           conversion; monotonic over the positive codes).
+* ``attention_fp8``     -- pinned through ``e4m3_decode`` and ``attention``, plus
+                           the descale invariances (Q and K descales act as a
+                           factor on the score scale, the V descale as a factor
+                           on O).
+* ``prob_weighted_abs`` -- pinned (V = 1 gives W = 1; identical keys give
+                           Pmax = 1/Nk; one-hot selection gives Pmax ~ 1 and
+                           W = |selected V row|; brute force on a tiny case).
 """
 from .attention import (  # noqa: F401
     attention,
@@ -29,3 +39,4 @@ from .attention import (  # noqa: F401
     split_bounds,
     splitkv_partials,
 )
+from .fp8 import attention_fp8, e4m3_decode, e4m3_value, prob_weighted_abs  # noqa: F401

@@ -18,6 +18,13 @@ Recipe (stated once, used everywhere):
   normal draw is always finite).  The fp32 debug path uses the unrounded draws.
 * Q has shape [B, Hq, Nq, d]; K and V have shape [B, Hkv, Nk, d]; all are
   contiguous row-major with d innermost.
+* The fp8 inputs are the same fp32 draws divided by a fixed per-tensor
+  descale factor (``FP8_DESCALE``: 6.75/448 for Q, 6.5/448 for K, 6.25/448
+  for V, so a draw of about 6.5 standard deviations maps to the largest
+  finite value 448) and encoded as OCP E4M3 (1 sign, 4 exponent bits with
+  bias 7, 3 mantissa bits, subnormals, no infinities) with round to nearest,
+  ties to even; the rare magnitudes beyond 448 saturate to +-448.  The value a
+  byte stands for is (its E4M3 value) * descale.
 """
 from __future__ import annotations
 
@@ -88,6 +95,9 @@ WORKLOADS = {
         "batched_prefill_b4h16_n2048_causal", 4, 16, 16, 2048, 2048, 128, causal=True),
     "pages_shape_h8_q4096_kv8192": Workload("pages_shape_h8_q4096_kv8192", 1, 8, 8, 4096, 8192, 128),
     "long_causal_h32_n16384": Workload("long_causal_h32_n16384", 1, 32, 32, 16384, 16384, 128, causal=True),
+    "pages_shape_fp8_h8_q4096_kv8192": Workload(
+        "pages_shape_fp8_h8_q4096_kv8192", 1, 8, 8, 4096, 8192, 128,
+        note="the pages' shape with OCP E4M3 inputs and per-tensor descale factors"),
     "gqa_decode_b64_hq32_hkv8_kv8192": Workload(
         "gqa_decode_b64_hq32_hkv8_kv8192", 64, 32, 8, 1, 8192, 128, num_splits=16),
 }
@@ -108,6 +118,36 @@ def bf16_bits(x: np.ndarray) -> np.ndarray:
 def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
     """Exact widening of bf16 bit patterns to fp32."""
     return (np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+# Per-tensor descale factors of the fp8 inputs (Q, K, V).
+FP8_DESCALE = (6.75 / 448.0, 6.5 / 448.0, 6.25 / 448.0)
+
+
+def e4m3_bits(x: np.ndarray) -> np.ndarray:
+    """Encode finite values as OCP E4M3 bytes (round to nearest, ties to even;
+    magnitudes above 448 saturate to 448).  Returns uint8 codes, never the
+    NaN codes 0x7F / 0xFF."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.minimum(np.abs(x), 448.0)
+    # Spacing of representable values around a: 2^(e-3) for a in [2^e, 2^(e+1)),
+    # e >= -6; below 2^-6 the subnormal spacing 2^-9.
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.maximum(e, -6.0)
+    quantum = np.exp2(e - 3.0)
+    r = np.rint(a / quantum) * quantum  # rint: ties to even (exact: quantum is a power of two)
+    r = np.minimum(r, 448.0)
+    code = np.zeros(a.shape, dtype=np.int64)
+    sub = r < 2.0 ** -6
+    code[sub] = np.rint(r[sub] / 2.0 ** -9).astype(np.int64)
+    nrm = ~sub
+    with np.errstate(divide="ignore"):
+        en = np.floor(np.log2(np.where(nrm, r, 1.0)))
+    mant = np.rint((r / np.exp2(en) - 1.0) * 8.0).astype(np.int64)
+    code[nrm] = ((en[nrm].astype(np.int64) + 7) << 3) | mant[nrm]
+    sign = np.signbit(x).astype(np.int64) << 7
+    return (code | sign).astype(np.uint8)
 
 
 def _threads() -> int:
@@ -150,6 +190,27 @@ def draw_bf16(seed: int, tensor: int, shape, heads=None, rows=None) -> np.ndarra
     def one(bh):
         s = _slab(seed, tensor, bh[0], bh[1], N, d)
         return bf16_bits(s if rows is None else s[rows])
+
+    if len(pairs) > 4:
+        with ThreadPoolExecutor(_threads()) as ex:
+            slabs = list(ex.map(one, pairs))
+    else:
+        slabs = [one(p) for p in pairs]
+    out = np.stack(slabs, axis=0)
+    if heads is None:
+        out = out.reshape(B, H, out.shape[-2], d)
+    return out
+
+
+def draw_e4m3(seed: int, tensor: int, shape, heads=None, rows=None) -> np.ndarray:
+    """E4M3 codes (uint8) of :func:`draw` divided by ``FP8_DESCALE[tensor]``."""
+    B, H, N, d = shape
+    pairs = [(b, h) for b in range(B) for h in range(H)] if heads is None else list(heads)
+    ds = FP8_DESCALE[tensor]
+
+    def one(bh):
+        s = _slab(seed, tensor, bh[0], bh[1], N, d)
+        return e4m3_bits((s if rows is None else s[rows]).astype(np.float64) / ds)
 
     if len(pairs) > 4:
         with ThreadPoolExecutor(_threads()) as ex:
