@@ -5,11 +5,12 @@ library's HIP kernels. torch supplies device memory and streams. If the library
 is not built, loading it raises; there is no fallback path.
 
 Entry points with the C names (tensors in, status checked, nothing returned):
-    fa_fwd, fa_fwd_fp32, fa_fwd_splitkv, fa_fwd_splitkv_paged, fa_combine,
+    fa_fwd, fa_fwd_fp32, fa_fwd_fp8, fa_fwd_splitkv, fa_fwd_splitkv_paged, fa_combine,
     fa_splitkv_workspace_bytes, fa_status_str
 Convenience wrappers that allocate the outputs:
     forward(q, k, v, causal=False, scale=None)            -> (o, lse)
     forward_fp32(q, k, v, causal=False, scale=None)       -> (o, lse)
+    forward_fp8(q8, k8, v8, descale, causal=False, scale=None) -> (o, lse)
     decode(q, k, v, num_splits, causal=False, scale=None, workspace=None) -> (o, lse)
     decode_paged(q, k_cache, v_cache, block_table, seq_lens, num_splits, ...) -> (o, lse)
 """
@@ -31,6 +32,7 @@ _P, _I, _F, _S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
 SIGNATURES = {
     "fa_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P]),
     "fa_fwd_fp32": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "fa_fwd_fp8": (_I, [_P, _P, _P, _F, _F, _F, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P]),
     "fa_splitkv_workspace_bytes": (_S, [_I, _I, _I, _I, _I]),
     "fa_fwd_splitkv": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _P, _S, _P]),
     "fa_combine": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
@@ -196,6 +198,40 @@ def fa_combine(o_part, lse_part, o, lse, stream=None):
         raise ValueError("o must be bf16 [B, Hq, Nq, d] and lse [B, Hq, Nq]")
     st = lib().fa_combine(_ptr(o_part), _ptr(lse_part), _ptr(o), _ptr(lse), B, Hq, Nq, d, S, _stream(stream))
     _check("fa_combine", st)
+
+
+def _fp8_view(t, name):
+    """E4M3 tensors travel as uint8 bytes; torch's float8_e4m3fn is accepted too."""
+    import torch
+    if t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8)
+    if t.dtype != torch.uint8:
+        raise TypeError(f"{name} must be uint8 E4M3 codes or float8_e4m3fn, got {t.dtype}")
+    return t
+
+
+def fa_fwd_fp8(q, k, v, o, lse, descale, scale=None, causal=False, stream=None):
+    """fp8 (E4M3, per-tensor descale) forward into caller-provided o (bf16
+    [B,Hq,Nq,d]) and lse (fp32 [B,Hq,Nq]); descale = (q, k, v) factors."""
+    import torch
+    q, k, v = _fp8_view(q, "q"), _fp8_view(k, "k"), _fp8_view(v, "v")
+    B, Hq, Hkv, Nq, Nk, d = _dims(q, k, v, torch.uint8)
+    if o.dtype != torch.bfloat16 or tuple(o.shape) != tuple(q.shape) or not o.is_contiguous():
+        raise ValueError("o must be a contiguous bf16 tensor shaped like q")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != tuple(q.shape[:3]) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, Hq, Nq] tensor")
+    qd, kd, vd = (float(x) for x in descale)
+    st = lib().fa_fwd_fp8(_ptr(q), _ptr(k), _ptr(v), qd, kd, vd, _ptr(o), _ptr(lse), B, Hq, Hkv, Nq, Nk, d,
+                          _default_scale(d, scale), int(bool(causal)), _stream(stream))
+    _check("fa_fwd_fp8", st)
+
+
+def forward_fp8(q, k, v, descale, causal=False, scale=None, stream=None):
+    import torch
+    o = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    fa_fwd_fp8(q, k, v, o, lse, descale, scale=scale, causal=causal, stream=stream)
+    return o, lse
 
 
 def forward(q, k, v, causal=False, scale=None, stream=None):

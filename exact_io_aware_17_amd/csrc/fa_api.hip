@@ -96,6 +96,23 @@ fa_status fa_fwd_fp32(const float* q, const float* k, const float* v, float* o, 
   return launched(fa::launch_fwd_fp32(a));
 }
 
+fa_status fa_fwd_fp8(const void* q, const void* k, const void* v, float q_descale, float k_descale,
+                     float v_descale, void* o, float* lse, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                     float scale, int causal, void* stream) {
+  fa_status st = check_common(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal);
+  if (st != FA_OK) return st;
+  if (d != 128) return FA_ERR_UNSUPPORTED;
+  for (float x : {q_descale, k_descale, v_descale})
+    if (!(x > 0.f) || !isfinite(x)) return FA_ERR_ARG;
+  // The score scale the kernel uses (scale * q_descale * k_descale * log2 e)
+  // must be a finite, non-zero fp32 value.
+  const double sl2 = (double)scale * q_descale * k_descale * 1.4426950408889634;
+  if (!(sl2 >= 1.1754943508222875e-38) || !(sl2 <= 3.4028234663852886e38)) return FA_ERR_ARG;
+  if (fa::fwd_fp8_grid(B, Hq, Nq) > kMaxGridX) return FA_ERR_UNSUPPORTED;
+  fa::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal, stream};
+  return launched(fa::launch_fwd_fp8(a, q_descale, k_descale, v_descale));
+}
+
 size_t fa_splitkv_workspace_bytes(int B, int Hq, int Nq, int d, int num_splits) {
   size_t ob = 0, total = 0;
   if (!split_ws_sizes(B, Hq, Nq, d, num_splits, &ob, &total)) return 0;

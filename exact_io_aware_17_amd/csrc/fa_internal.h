@@ -42,6 +42,8 @@ struct CombineArgs {
 
 hipError_t launch_fwd_bf16(const FwdArgs& a);
 hipError_t launch_fwd_fp32(const FwdArgs& a);
+// q, k, v of `a` are E4M3 bytes (d = 128); o is bf16, lse fp32.
+hipError_t launch_fwd_fp8(const FwdArgs& a, float q_descale, float k_descale, float v_descale);
 hipError_t launch_splitkv_partial(const SplitArgs& a);
 hipError_t launch_combine(const CombineArgs& a);
 
@@ -49,6 +51,7 @@ hipError_t launch_combine(const CombineArgs& a);
 // against the hardware limit before launching.
 long fwd_bf16_grid(int B, int Hq, int Nq);
 long fwd_fp32_grid(int B, int Hq, int Nq);
+long fwd_fp8_grid(int B, int Hq, int Nq);
 long splitkv_grid(int B, int Hq, int Hkv, int Nq, int num_splits);
 long combine_grid(int B, int Hq, int Nq);
 

@@ -79,6 +79,32 @@ fa_status fa_fwd_fp32(const float* q, const float* k, const float* v, float* o, 
                       float scale, int causal, void* stream);
 
 /*
+ * fa_fwd_fp8 -- attention forward over 8-bit inputs.  The pages name MXFP8
+ * matrix instructions as the reason to write the kernel by hand ("Flash
+ * Attention on the 5090 in CUDA C++", the goal at the top and "What next")
+ * and low-precision paths as FlashAttention-3's direction ("Flash Attention",
+ * aiunderstanding.org, FAQ), without fixing a format.  Reading taken here:
+ * q [B,Hq,Nq,d], k/v [B,Hkv,Nk,d] are OCP E4M3 bytes (bias 7, no
+ * infinities, 0x7F/0xFF NaN) with one descale factor per tensor; element x
+ * stands for e4m3(x) * descale.  The operation is exactly the one above on
+ * those values: S = (Q K^T) * scale, O = softmax(S) V, LSE as for fa_fwd.
+ * o [B,Hq,Nq,d] bf16 out, lse [B,Hq,Nq] fp32 out.
+ * Arithmetic: both products on fp8 matrix cores with fp32 accumulation; the
+ * softmax in fp32; probabilities rounded to E4M3 (nearest even) for P.V, the
+ * row sums taken before that rounding.  So LSE is as accurate as for bf16,
+ * and each O element is within about 2^-4 * sum_j P_ij |V_j| of the exact
+ * value (E4M3 keeps 3 mantissa bits).
+ * d must be 128 (64 returns FA_ERR_UNSUPPORTED).  Descales must be finite
+ * and > 0, and scale * q_descale * k_descale * log2(e) a normal fp32 value,
+ * else FA_ERR_ARG.  Other rules as fa_fwd (16-byte alignment of every
+ * pointer, 128-byte rows).  NaN inputs are out of contract.
+ */
+fa_status fa_fwd_fp8(const void* q, const void* k, const void* v,
+                     float q_descale, float k_descale, float v_descale,
+                     void* o, float* lse, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                     float scale, int causal, void* stream);
+
+/*
  * fa_splitkv_workspace_bytes -- bytes of workspace fa_fwd_splitkv needs:
  * partial outputs O_s [B,Hq,S,Nq,d] fp32 followed (at the next 256-byte
  * boundary) by partial LSE_s [B,Hq,S,Nq] fp32.  Returns 0 for invalid sizes.

@@ -28,7 +28,7 @@ def _declarations():
 
 def test_header_declarations_found():
     d = _declarations()
-    assert set(d) == {"fa_fwd", "fa_fwd_fp32", "fa_splitkv_workspace_bytes", "fa_fwd_splitkv",
+    assert set(d) == {"fa_fwd", "fa_fwd_fp32", "fa_fwd_fp8", "fa_splitkv_workspace_bytes", "fa_fwd_splitkv",
                       "fa_fwd_splitkv_paged", "fa_combine", "fa_status_str"}
 
 
@@ -69,6 +69,30 @@ def test_forward_argument_checks(entry):
         assert f(scale=s) == 7, s
     assert f(causal=2) == 7
     assert f(causal=-1) == 7
+
+
+def _fwd8(q=P, k=P, v=P, o=P, lse=P, ds=(0.01, 0.01, 0.01), B=1, Hq=2, Hkv=1, Nq=16, Nk=16, d=128, scale=0.1,
+          causal=0):
+    return fa.lib().fa_fwd_fp8(q, k, v, ds[0], ds[1], ds[2], o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal, None)
+
+
+def test_fp8_argument_checks():
+    """Every rejected call returns before anything is launched (no GPU needed)."""
+    for name in ("q", "k", "v", "o", "lse"):
+        assert _fwd8(**{name: None}) == 1, name
+        assert _fwd8(**{name: P + 8}) == 4, name
+    assert _fwd8(Hq=3, Hkv=2) == 2
+    assert _fwd8(B=-1) == 2
+    assert _fwd8(d=64) == 3
+    assert _fwd8(d=96) == 3
+    for s in (0.0, -0.5, math.inf, math.nan):
+        assert _fwd8(scale=s) == 7, s
+    for ds in ((0.0, 1.0, 1.0), (1.0, -1.0, 1.0), (1.0, 1.0, math.nan), (1.0, math.inf, 1.0),
+               (1e-30, 1e-30, 1.0), (1e30, 1e30, 1.0)):
+        assert _fwd8(ds=ds) == 7, ds
+    assert _fwd8(causal=2) == 7
+    # Nothing to compute: accepted without a launch.
+    assert _fwd8(q=None, o=None, lse=None, B=0, k=None, v=None) == 0
 
 
 def test_empty_tensors_may_be_null_but_shapes_still_checked():
