@@ -5,10 +5,11 @@ d=128, bf16, non-causal) through fa_fwd, W warm-up steps then exactly K timed
 steps; one JSON line on stdout. The line also carries the split-KV decode
 workload (B=64, Hq=32, Hkv=8, Nk=8192, 16 splits) timed the same way, the
 same decode over a paged K/V cache (16-key pages in a random order), the
+pages' shape again with OCP E4M3 inputs through fa_fwd_fp8, the
 roofline of the dominant kernel, and the CPU oracle timed on a bounded sample.
 
   python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--all]
-  python bench.py --only prefill|decode|decode_paged --steps 3   (short runs under a profiler)
+  python bench.py --only prefill|prefill_fp8|decode|decode_paged --steps 3   (short runs under a profiler)
   python bench.py --copy-calib                       (plain copy of known size, for counter scaling)
 """
 from __future__ import annotations
@@ -30,8 +31,10 @@ import numpy as np  # noqa: E402
 import synth  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA, published
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
 PREFILL = "pages_shape_h8_q4096_kv8192"
+PREFILL_FP8 = "pages_shape_fp8_h8_q4096_kv8192"
 DECODE = "gqa_decode_b64_hq32_hkv8_kv8192"
 OTHER_PREFILL = ["batched_prefill_b4h16_n2048", "batched_prefill_b4h16_n2048_causal", "long_causal_h32_n16384"]
 PROFILES = os.path.join(ROOT, "profiles")
@@ -51,6 +54,7 @@ def kernel_source_sha(files):
 
 
 FWD_SOURCES = ["fa_fwd.hip", "fa_common.h"]
+FWD8_SOURCES = ["fa_fwd_fp8.hip", "fa_common.h"]
 DEC_SOURCES = ["fa_splitkv.hip", "fa_common.h"]
 
 
@@ -112,6 +116,22 @@ def bench_prefill(w, steps, warmup, device, min_warm_s=0.2):
 
     def step():
         fa.fa_fwd(q, k, v, o, lse, scale=w.scale, causal=w.causal)
+    wall, ev_ms = time_steps(step, steps, warmup, min_warm_s)
+    return {"wall_s": wall, "ms_per_step": wall * 1e3 / steps, "kernel_ms": ev_ms,
+            "tflops": w.flops() / (wall / steps) / 1e12, "kernel_tflops": w.flops() / (ev_ms * 1e-3) / 1e12}
+
+
+def bench_prefill_fp8(w, steps, warmup, device, min_warm_s=0.2):
+    """fa_fwd_fp8 on E4M3 inputs (seeded draws / per-tensor descale)."""
+    import torch
+    import exact_io_aware_17_amd as fa
+    q, k, v = (torch.from_numpy(synth.draw_e4m3(w.seed, t, s)).to(device)
+               for t, s in ((synth.TENSOR_Q, w.q_shape), (synth.TENSOR_K, w.kv_shape), (synth.TENSOR_V, w.kv_shape)))
+    o = torch.empty(q.shape, dtype=torch.bfloat16, device=device)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=device)
+
+    def step():
+        fa.fa_fwd_fp8(q, k, v, o, lse, synth.FP8_DESCALE, scale=w.scale, causal=w.causal)
     wall, ev_ms = time_steps(step, steps, warmup, min_warm_s)
     return {"wall_s": wall, "ms_per_step": wall * 1e3 / steps, "kernel_ms": ev_ms,
             "tflops": w.flops() / (wall / steps) / 1e12, "kernel_tflops": w.flops() / (ev_ms * 1e-3) / 1e12}
@@ -233,7 +253,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--all", action="store_true", help="also time the other prefill workloads")
-    ap.add_argument("--only", choices=["prefill", "decode", "decode_paged"], default=None)
+    ap.add_argument("--only", choices=["prefill", "prefill_fp8", "decode", "decode_paged"], default=None)
     ap.add_argument("--copy-calib", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -258,6 +278,10 @@ def main():
         r = bench_prefill(wp, args.steps, args.warmup, device, min_warm_s=0.0)
         print(json.dumps({"only": "prefill", **r}))
         return
+    if args.only == "prefill_fp8":
+        r = bench_prefill_fp8(synth.WORKLOADS[PREFILL_FP8], args.steps, args.warmup, device, min_warm_s=0.0)
+        print(json.dumps({"only": "prefill_fp8", **r}))
+        return
     if args.only == "decode":
         r = bench_decode(wd, args.steps, args.warmup, device, min_warm_s=0.0)
         print(json.dumps({"only": "decode", **r}))
@@ -270,6 +294,10 @@ def main():
     log(f"prefill {wp.name}: warmup {args.warmup}, steps {args.steps}")
     rp = bench_prefill(wp, args.steps, args.warmup, device)
     log(f"  {rp}")
+    w8 = synth.WORKLOADS[PREFILL_FP8]
+    log(f"prefill fp8 {w8.name}: warmup {args.warmup}, steps {args.steps}")
+    r8 = bench_prefill_fp8(w8, args.steps, args.warmup, device)
+    log(f"  {r8}")
     log(f"decode {wd.name}: warmup {args.warmup}, steps {args.steps}")
     rd = bench_decode(wd, args.steps, args.warmup, device)
     log(f"  {rd}")
@@ -288,6 +316,7 @@ def main():
             log(f"  {others[name]}")
 
     fwd_traffic = traffic_from_profile("fwd_bf16_pages_shape_traffic.md", FWD_SOURCES)
+    fwd8_traffic = traffic_from_profile("fwd_fp8_pages_shape_traffic.md", FWD8_SOURCES)
     dec_traffic = traffic_from_profile("splitkv_decode_traffic.md", DEC_SOURCES)
     decp_traffic = traffic_from_profile("splitkv_paged_decode_traffic.md", DEC_SOURCES)
     line = {
@@ -309,6 +338,13 @@ def main():
                      "unit": "TFLOP/s", "frac": round(rp["kernel_tflops"] / PEAK_BF16_TFLOPS, 4),
                      "traffic": fwd_traffic, "kernel_ms": round(rp["kernel_ms"], 5),
                      "kernel": "fwd_bf16_kernel<128>"},
+        "prefill_fp8": {"workload": w8.name, "dtype": "fp8 e4m3 (per-tensor descale), bf16 out",
+                        "metric": "attention fwd TFLOPS (4*B*H*Nq*Nk*d per forward)", "value": round(r8["tflops"], 2),
+                        "unit": "TFLOP/s", "ms_per_step": round(r8["ms_per_step"], 5),
+                        "roofline": {"bound": "mfma", "achieved": round(r8["kernel_tflops"], 2),
+                                     "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                                     "frac": round(r8["kernel_tflops"] / PEAK_FP8_TFLOPS, 4), "traffic": fwd8_traffic,
+                                     "kernel_ms": round(r8["kernel_ms"], 5), "kernel": "fwd_fp8_kernel"}},
         "decode": {"workload": wd.name, "metric": "decode HBM GB/s (algorithmic bytes / step time)",
                    "value": round(rd["gbs"], 1), "unit": "GB/s", "ms_per_step": round(rd["ms_per_step"], 5),
                    "roofline": {"bound": "hbm", "achieved": round(rd["kernel_gbs"], 1), "peak": PEAK_HBM_GBS,
