@@ -64,11 +64,18 @@ constexpr float kF8SumHi = 448.f;
 constexpr int kF8MergeBytes = 4 * 4 * 16 * 64 * 4 + 2 * 4 * 64 * 4;
 constexpr int kF8Lds = kF8MergeBytes > 2 * kF8VBase ? kF8MergeBytes : 2 * kF8VBase;
 
-// 16-byte-chunk XOR swizzle of a 128-byte row: two rows share the 64 banks,
-// so the chunk is XORed with bits 1..3 of the row. Sixteen consecutive rows
-// read at one logical chunk, and the eight key rows of a transposing read
-// (rows r..r+3 and r+8..r+11, r a multiple of 4), land on distinct banks.
-__device__ __forceinline__ int swz8(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
+// 16-byte-chunk XOR swizzle of a 128-byte row. Two rows share the 64 banks
+// (odd rows on the upper 32), so the chunk is XORed with a bijection of row
+// bits 1..3: (bit 2, bit 1, bit 3) as (bit 0, bit 1, bit 2) of the XOR.
+//  * K operand reads (16 consecutive rows at one logical chunk per pass):
+//    the bijection puts the 8 even and the 8 odd rows on 8 distinct chunks.
+//  * Transposing V reads (one pass = 32 lanes: rows r..r+3 and r+8..r+11,
+//    r = 4 hl, at chunks 2 db and 2 db + 1): bits 1 and 3 of the row select
+//    the chunk pair, so the four even (and four odd) rows cover all eight
+//    chunks. Both are conflict-free (SQ_LDS_BANK_CONFLICT = 0).
+__device__ __forceinline__ int swz8(int row, int chunk) {
+  return chunk ^ (((row >> 2) & 1) | (((row >> 1) & 1) << 1) | (((row >> 3) & 1) << 2));
+}
 
 __device__ __forceinline__ f32x16 mfma_f8(const i32x8& a, const i32x8& b, const f32x16& c) {
   // Operand formats 0/0: E4M3 for A and B; no block scales.
