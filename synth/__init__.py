@@ -95,6 +95,9 @@ WORKLOADS = {
         "batched_prefill_b4h16_n2048_causal", 4, 16, 16, 2048, 2048, 128, causal=True),
     "pages_shape_h8_q4096_kv8192": Workload("pages_shape_h8_q4096_kv8192", 1, 8, 8, 4096, 8192, 128),
     "long_causal_h32_n16384": Workload("long_causal_h32_n16384", 1, 32, 32, 16384, 16384, 128, causal=True),
+    "pages_shape_d256_h8_q4096_kv8192": Workload(
+        "pages_shape_d256_h8_q4096_kv8192", 1, 8, 8, 4096, 8192, 256,
+        note="the pages' shape at head size 256"),
     "pages_shape_fp8_h8_q4096_kv8192": Workload(
         "pages_shape_fp8_h8_q4096_kv8192", 1, 8, 8, 4096, 8192, 128,
         note="the pages' shape with OCP E4M3 inputs and per-tensor descale factors"),

@@ -66,6 +66,45 @@ def test_fp32_full_oracle(w):
     assert_close(errors(o, o_ref, lse, lse_ref), F32_TOL, F32_TOL, what=w.name + " fp32")
 
 
+D256 = [
+    synth.Workload("d256_single_head_n256", 1, 1, 1, 256, 256, 256),
+    synth.Workload("d256_ragged_gqa", 2, 4, 2, 200, 333, 256, seed=1),
+    synth.Workload("d256_ragged_gqa_causal", 2, 4, 2, 200, 333, 256, causal=True, seed=2),
+    synth.Workload("d256_more_queries_than_keys_causal", 1, 3, 1, 300, 70, 256, causal=True, seed=5),
+    synth.Workload("d256_one_query_one_key", 1, 1, 1, 1, 1, 256),
+    synth.Workload("d256_keys_below_one_tile", 1, 2, 2, 300, 17, 256, seed=4),
+    synth.Workload("d256_square_causal", 1, 2, 2, 384, 384, 256, causal=True),
+    synth.Workload("d256_odd_tiles_causal", 1, 2, 1, 161, 161, 256, causal=True, seed=6),
+    # 8 x 64 heads x 2 query blocks = 1024 workgroups: the one-group layout.
+    synth.Workload("d256_many_blocks_gqa_causal_ragged", 8, 64, 8, 130, 77, 256, causal=True, seed=7),
+    synth.Workload("d256_many_blocks_ragged", 4, 64, 16, 200, 90, 256, seed=8),
+]
+
+
+@pytest.mark.parametrize("w", D256, ids=lambda w: w.name)
+def test_bf16_d256_full_oracle(w):
+    """Head size 256 (fa_fwd's d = 256 kernel) against the oracle."""
+    say(f"case bf16 d256 full {w.name}")
+    o, lse = _run_fwd(w)
+    o_ref, lse_ref = oracle_full(w)
+    assert_close(errors(o, o_ref, lse, lse_ref), what=w.name)
+
+
+@pytest.mark.parametrize("name", ["pages_shape_d256_h8_q4096_kv8192", "batched_d256_b4h16_n2048",
+                                  "batched_d256_b4h16_n2048_causal"])
+def test_bf16_d256_full_size_sampled(name):
+    """Full-size d = 256 launches: the pages' shape (256 workgroups, the
+    two-group layout) and the batched shape (1024, the one-group layout)."""
+    w = W.get(name) or synth.Workload(name, 4, 16, 16, 2048, 2048, 256, causal=name.endswith("causal"))
+    say(f"case bf16 d256 full-size {w.name}")
+    o, lse = _run_fwd(w)
+    rows = sample_rows(w.Nq)
+    heads = [(0, 0), (w.B - 1, w.Hq - 3)]
+    o_ref, lse_ref = oracle_sample(w, heads, rows)
+    for n, (b, h) in enumerate(heads):
+        assert_close(errors(o[b, h, rows], o_ref[n], lse[b, h, rows], lse_ref[n]), what=f"{w.name} head {h}")
+
+
 LARGE = ["batched_prefill_b4h16_n2048", "batched_prefill_b4h16_n2048_causal", "pages_shape_h8_q4096_kv8192",
          "long_causal_h32_n16384"]
 
