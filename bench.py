@@ -5,11 +5,12 @@ d=128, bf16, non-causal) through fa_fwd, W warm-up steps then exactly K timed
 steps; one JSON line on stdout. The line also carries the split-KV decode
 workload (B=64, Hq=32, Hkv=8, Nk=8192, 16 splits) timed the same way, the
 same decode over a paged K/V cache (16-key pages in a random order), the
-pages' shape again with OCP E4M3 inputs through fa_fwd_fp8, the
+pages' shape again with OCP E4M3 inputs through fa_fwd_fp8 and at head
+size 256 through fa_fwd, the
 roofline of the dominant kernel, and the CPU oracle timed on a bounded sample.
 
   python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--all]
-  python bench.py --only prefill|prefill_fp8|decode|decode_paged --steps 3   (short runs under a profiler)
+  python bench.py --only prefill|prefill_fp8|prefill_d256|decode|decode_paged --steps 3   (short runs under a profiler)
   python bench.py --copy-calib                       (plain copy of known size, for counter scaling)
 """
 from __future__ import annotations
@@ -35,6 +36,7 @@ PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA, published
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
 PREFILL = "pages_shape_h8_q4096_kv8192"
 PREFILL_FP8 = "pages_shape_fp8_h8_q4096_kv8192"
+PREFILL_D256 = "pages_shape_d256_h8_q4096_kv8192"
 DECODE = "gqa_decode_b64_hq32_hkv8_kv8192"
 OTHER_PREFILL = ["batched_prefill_b4h16_n2048", "batched_prefill_b4h16_n2048_causal", "long_causal_h32_n16384"]
 PROFILES = os.path.join(ROOT, "profiles")
@@ -55,6 +57,7 @@ def kernel_source_sha(files):
 
 FWD_SOURCES = ["fa_fwd.hip", "fa_common.h"]
 FWD8_SOURCES = ["fa_fwd_fp8.hip", "fa_common.h"]
+FWD256_SOURCES = ["fa_fwd_d256.hip", "fa_common.h"]
 DEC_SOURCES = ["fa_splitkv.hip", "fa_common.h"]
 
 
@@ -253,7 +256,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--all", action="store_true", help="also time the other prefill workloads")
-    ap.add_argument("--only", choices=["prefill", "prefill_fp8", "decode", "decode_paged"], default=None)
+    ap.add_argument("--only", choices=["prefill", "prefill_fp8", "prefill_d256", "decode", "decode_paged"],
+                    default=None)
     ap.add_argument("--copy-calib", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -278,6 +282,10 @@ def main():
         r = bench_prefill(wp, args.steps, args.warmup, device, min_warm_s=0.0)
         print(json.dumps({"only": "prefill", **r}))
         return
+    if args.only == "prefill_d256":
+        r = bench_prefill(synth.WORKLOADS[PREFILL_D256], args.steps, args.warmup, device, min_warm_s=0.0)
+        print(json.dumps({"only": "prefill_d256", **r}))
+        return
     if args.only == "prefill_fp8":
         r = bench_prefill_fp8(synth.WORKLOADS[PREFILL_FP8], args.steps, args.warmup, device, min_warm_s=0.0)
         print(json.dumps({"only": "prefill_fp8", **r}))
@@ -298,6 +306,10 @@ def main():
     log(f"prefill fp8 {w8.name}: warmup {args.warmup}, steps {args.steps}")
     r8 = bench_prefill_fp8(w8, args.steps, args.warmup, device)
     log(f"  {r8}")
+    w256 = synth.WORKLOADS[PREFILL_D256]
+    log(f"prefill d256 {w256.name}: warmup {args.warmup}, steps {args.steps}")
+    r256 = bench_prefill(w256, args.steps, args.warmup, device)
+    log(f"  {r256}")
     log(f"decode {wd.name}: warmup {args.warmup}, steps {args.steps}")
     rd = bench_decode(wd, args.steps, args.warmup, device)
     log(f"  {rd}")
@@ -317,6 +329,7 @@ def main():
 
     fwd_traffic = traffic_from_profile("fwd_bf16_pages_shape_traffic.md", FWD_SOURCES)
     fwd8_traffic = traffic_from_profile("fwd_fp8_pages_shape_traffic.md", FWD8_SOURCES)
+    fwd256_traffic = traffic_from_profile("fwd_bf16_d256_pages_shape_traffic.md", FWD256_SOURCES)
     dec_traffic = traffic_from_profile("splitkv_decode_traffic.md", DEC_SOURCES)
     decp_traffic = traffic_from_profile("splitkv_paged_decode_traffic.md", DEC_SOURCES)
     line = {
@@ -345,6 +358,15 @@ def main():
                                      "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                                      "frac": round(r8["kernel_tflops"] / PEAK_FP8_TFLOPS, 4), "traffic": fwd8_traffic,
                                      "kernel_ms": round(r8["kernel_ms"], 5), "kernel": "fwd_fp8_kernel"}},
+        "prefill_d256": {"workload": w256.name, "dtype": "bf16", "d": 256,
+                         "metric": "attention fwd TFLOPS (4*B*H*Nq*Nk*d per forward)",
+                         "value": round(r256["tflops"], 2), "unit": "TFLOP/s",
+                         "ms_per_step": round(r256["ms_per_step"], 5),
+                         "roofline": {"bound": "mfma", "achieved": round(r256["kernel_tflops"], 2),
+                                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                                      "frac": round(r256["kernel_tflops"] / PEAK_BF16_TFLOPS, 4),
+                                      "traffic": fwd256_traffic, "kernel_ms": round(r256["kernel_ms"], 5),
+                                      "kernel": "fwd_bf16_d256_kernel<2>"}},
         "decode": {"workload": wd.name, "metric": "decode HBM GB/s (algorithmic bytes / step time)",
                    "value": round(rd["gbs"], 1), "unit": "GB/s", "ms_per_step": round(rd["ms_per_step"], 5),
                    "roofline": {"bound": "hbm", "achieved": round(rd["kernel_gbs"], 1), "peak": PEAK_HBM_GBS,
