@@ -26,6 +26,11 @@ Parity status of each function (the pins live in tests/test_oracle.py):
                            the descale invariances (Q and K descales act as a
                            factor on the score scale, the V descale as a factor
                            on O).
+* ``attention_backward`` -- pinned (central finite differences of <O, dO>
+                           on tiny cases, torch autograd of the float64
+                           definition with the same mask, the identities
+                           sum_j dK_j = 0 and sum_j dV_j = sum_i dO_i, V = 1
+                           giving dQ = dK = 0, D = rowsum(dO * O)).
 * ``prob_weighted_abs`` -- pinned (V = 1 gives W = 1; identical keys give
                            Pmax = 1/Nk; one-hot selection gives Pmax ~ 1 and
                            W = |selected V row|; brute force on a tiny case).
@@ -39,4 +44,5 @@ from .attention import (  # noqa: F401
     split_bounds,
     splitkv_partials,
 )
+from .backward import attention_backward  # noqa: F401
 from .fp8 import attention_fp8, e4m3_decode, e4m3_value, prob_weighted_abs  # noqa: F401
