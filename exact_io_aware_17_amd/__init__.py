@@ -5,12 +5,13 @@ library's HIP kernels. torch supplies device memory and streams. If the library
 is not built, loading it raises; there is no fallback path.
 
 Entry points with the C names (tensors in, status checked, nothing returned):
-    fa_fwd, fa_fwd_fp32, fa_fwd_fp8, fa_fwd_splitkv, fa_fwd_splitkv_paged, fa_combine,
+    fa_fwd, fa_fwd_fp32, fa_fwd_fp8, fa_bwd, fa_bwd_workspace_bytes, fa_fwd_splitkv, fa_fwd_splitkv_paged, fa_combine,
     fa_splitkv_workspace_bytes, fa_status_str
 Convenience wrappers that allocate the outputs:
     forward(q, k, v, causal=False, scale=None)            -> (o, lse)
     forward_fp32(q, k, v, causal=False, scale=None)       -> (o, lse)
     forward_fp8(q8, k8, v8, descale, causal=False, scale=None) -> (o, lse)
+    backward(q, k, v, o, lse, dout, causal=False, scale=None) -> (dq, dk, dv)
     decode(q, k, v, num_splits, causal=False, scale=None, workspace=None) -> (o, lse)
     decode_paged(q, k_cache, v_cache, block_table, seq_lens, num_splits, ...) -> (o, lse)
 """
@@ -33,6 +34,8 @@ SIGNATURES = {
     "fa_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P]),
     "fa_fwd_fp32": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P]),
     "fa_fwd_fp8": (_I, [_P, _P, _P, _F, _F, _F, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "fa_bwd_workspace_bytes": (_S, [_I, _I, _I, _I]),
+    "fa_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P, _S, _P]),
     "fa_splitkv_workspace_bytes": (_S, [_I, _I, _I, _I, _I]),
     "fa_fwd_splitkv": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _P, _S, _P]),
     "fa_combine": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
@@ -232,6 +235,35 @@ def forward_fp8(q, k, v, descale, causal=False, scale=None, stream=None):
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
     fa_fwd_fp8(q, k, v, o, lse, descale, scale=scale, causal=causal, stream=stream)
     return o, lse
+
+
+def fa_bwd_workspace_bytes(B, Hq, Nq, d) -> int:
+    return int(lib().fa_bwd_workspace_bytes(B, Hq, Nq, d))
+
+
+def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, scale=None, causal=False, stream=None):
+    """Backward into caller-provided dq (like q), dk, dv (like k) bf16 tensors."""
+    import torch
+    B, Hq, Hkv, Nq, Nk, d = _dims(q, k, v, torch.bfloat16)
+    for name, t, like in (("o", o, q), ("dout", dout, q), ("dq", dq, q), ("dk", dk, k), ("dv", dv, k)):
+        if t.dtype != torch.bfloat16 or tuple(t.shape) != tuple(like.shape) or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous bf16 tensor shaped like {'q' if like is q else 'k'}")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != tuple(q.shape[:3]) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, Hq, Nq] tensor")
+    st = lib().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+                      B, Hq, Hkv, Nq, Nk, d, _default_scale(d, scale), int(bool(causal)), _ptr(workspace),
+                      workspace.numel() * workspace.element_size() if workspace is not None else 0, _stream(stream))
+    _check("fa_bwd", st)
+
+
+def backward(q, k, v, o, lse, dout, causal=False, scale=None, workspace=None, stream=None):
+    import torch
+    B, Hq, Nq, d = q.shape
+    if workspace is None:
+        workspace = torch.empty(max(fa_bwd_workspace_bytes(B, Hq, Nq, d), 256), dtype=torch.uint8, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, scale=scale, causal=causal, stream=stream)
+    return dq, dk, dv
 
 
 def forward(q, k, v, causal=False, scale=None, stream=None):

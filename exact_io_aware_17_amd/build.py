@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libfa.so")
-SOURCES = ["fa_api.hip", "fa_fwd.hip", "fa_fwd_d256.hip", "fa_fwd_fp8.hip", "fa_fp32.hip", "fa_splitkv.hip"]
+SOURCES = ["fa_api.hip", "fa_fwd.hip", "fa_fwd_d256.hip", "fa_fwd_fp8.hip", "fa_fp32.hip", "fa_splitkv.hip", "fa_bwd.hip"]
 ARCH = "gfx950"
 
 # Packed-fp32 VALU forms are kept out of the generated code.

@@ -40,6 +40,18 @@ struct CombineArgs {
   void* stream;
 };
 
+// Backward: f carries q, k, v, the forward's lse, sizes, scale, mask, stream.
+struct BwdArgs {
+  FwdArgs f;
+  const void* o;     // forward output [B, Hq, Nq, d] bf16
+  const void* dout;  // dO [B, Hq, Nq, d] bf16
+  void* dq;          // [B, Hq, Nq, d] bf16
+  void* dk;          // [B, Hkv, Nk, d] bf16
+  void* dv;          // [B, Hkv, Nk, d] bf16
+  float* dq_acc;     // workspace: fp32 [B, Hq, Nq, d]
+  float* dsum;       // workspace: fp32 [B, Hq, Nq]
+};
+
 hipError_t launch_fwd_bf16(const FwdArgs& a);       // d = 64, 128
 hipError_t launch_fwd_bf16_d256(const FwdArgs& a);  // d = 256
 hipError_t launch_fwd_fp32(const FwdArgs& a);
@@ -47,6 +59,7 @@ hipError_t launch_fwd_fp32(const FwdArgs& a);
 hipError_t launch_fwd_fp8(const FwdArgs& a, float q_descale, float k_descale, float v_descale);
 hipError_t launch_splitkv_partial(const SplitArgs& a);
 hipError_t launch_combine(const CombineArgs& a);
+hipError_t launch_bwd(const BwdArgs& a);
 
 // Grid sizes (workgroups) the launchers would use; the ABI layer checks them
 // against the hardware limit before launching.
@@ -55,5 +68,6 @@ long fwd_fp32_grid(int B, int Hq, int Nq);
 long fwd_fp8_grid(int B, int Hq, int Nq);
 long splitkv_grid(int B, int Hq, int Hkv, int Nq, int num_splits);
 long combine_grid(int B, int Hq, int Nq);
+long bwd_grid(int B, int Hkv, int Nk);
 
 }  // namespace fa

@@ -108,6 +108,38 @@ fa_status fa_fwd_fp8(const void* q, const void* k, const void* v,
                      float scale, int causal, void* stream);
 
 /*
+ * fa_bwd_workspace_bytes -- bytes of workspace fa_bwd needs: an fp32 dQ
+ * accumulator [B,Hq,Nq,d] followed (at the next 256-byte boundary) by the
+ * fp32 row sums D [B,Hq,Nq].  Returns 0 for invalid sizes.
+ */
+size_t fa_bwd_workspace_bytes(int B, int Hq, int Nq, int d);
+
+/*
+ * fa_bwd -- gradients of the bf16 forward.  The pages name the backward pass
+ * and training use ("Flash Attention", aiunderstanding.org) but print no
+ * algorithm for it; what is computed is the chain rule through the forward
+ * definition above.  With dO = dout the gradient of a loss with respect to
+ * O, P = exp(S - LSE) recomputed from the forward's lse, and
+ * D_i = sum_c dO_ic O_ic:
+ *     dV = P^T dO,   dS = P * (dO V^T - D),   dQ = dS K * scale,
+ *     dK = dS^T Q * scale,
+ * with dK, dV of a KV head summed over its query heads (GQA) and masked
+ * entries contributing nothing (a query row without keys gets dQ = 0).
+ * q, o, dout, dq [B,Hq,Nq,d] bf16; k, v, dk, dv [B,Hkv,Nk,d] bf16; lse
+ * [B,Hq,Nq] fp32 as written by fa_fwd with the same q, k, v, scale, causal.
+ * Products run on bf16 matrix cores with fp32 accumulation; P and dS are
+ * rounded to bf16 as MFMA operands, D and the softmax are fp32, dQ is
+ * accumulated in fp32 in the workspace before its bf16 rounding.
+ * d must be 64 or 128.  workspace (device, caller-owned, 256-byte aligned)
+ * of at least fa_bwd_workspace_bytes(B,Hq,Nq,d) bytes; its contents are
+ * overwritten.  Other rules as fa_fwd; outputs must not overlap the inputs.
+ */
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                 const float* lse, void* dq, void* dk, void* dv,
+                 int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * fa_splitkv_workspace_bytes -- bytes of workspace fa_fwd_splitkv needs:
  * partial outputs O_s [B,Hq,S,Nq,d] fp32 followed (at the next 256-byte
  * boundary) by partial LSE_s [B,Hq,S,Nq] fp32.  Returns 0 for invalid sizes.

@@ -8,7 +8,7 @@ named workload shapes.
 Recipe (stated once, used everywhere):
 
 * Every tensor is a set of independent (batch, head) slabs of shape (N, d).
-  Slab (b, h) of tensor ``t`` (0 = Q, 1 = K, 2 = V) is drawn as
+  Slab (b, h) of tensor ``t`` (0 = Q, 1 = K, 2 = V, 3 = dO) is drawn as
   ``standard_normal((N, d), float32)`` from a PCG64 generator seeded with
   ``SeedSequence([seed, t, b, h])``.  Slabs can therefore be drawn one at a
   time (for sampled checks of large workloads) or in parallel threads, and the
@@ -36,6 +36,7 @@ from dataclasses import dataclass, field
 import numpy as np
 
 TENSOR_Q, TENSOR_K, TENSOR_V = 0, 1, 2
+TENSOR_DO = 3  # the output gradient dO of the backward pass
 
 
 @dataclass(frozen=True)

@@ -28,7 +28,8 @@ def _declarations():
 
 def test_header_declarations_found():
     d = _declarations()
-    assert set(d) == {"fa_fwd", "fa_fwd_fp32", "fa_fwd_fp8", "fa_splitkv_workspace_bytes", "fa_fwd_splitkv",
+    assert set(d) == {"fa_fwd", "fa_fwd_fp32", "fa_fwd_fp8", "fa_bwd", "fa_bwd_workspace_bytes",
+                      "fa_splitkv_workspace_bytes", "fa_fwd_splitkv",
                       "fa_fwd_splitkv_paged", "fa_combine", "fa_status_str"}
 
 
@@ -95,6 +96,31 @@ def test_fp8_argument_checks():
     assert _fwd8(causal=2) == 7
     # Nothing to compute: accepted without a launch.
     assert _fwd8(q=None, o=None, lse=None, B=0, k=None, v=None) == 0
+
+
+def test_bwd_workspace_and_argument_checks():
+    """Host-side checks of fa_bwd; every rejected call returns before a launch."""
+    lib = fa.lib()
+    assert lib.fa_bwd_workspace_bytes(2, 3, 5, 128) == 15360 + 256  # 30 rows * 128 * 4, then 30 * 4 rounded up to 256
+    assert lib.fa_bwd_workspace_bytes(1, 1, 0, 64) == 0 + 0
+    assert lib.fa_bwd_workspace_bytes(1, 1, 4, 96) == 0
+    assert lib.fa_bwd_workspace_bytes(-1, 1, 4, 64) == 0
+
+    def f(q=P, k=P, v=P, o=P, do=P, lse=P, dq=P, dk=P, dv=P, B=1, Hq=2, Hkv=1, Nq=16, Nk=16, d=128, scale=0.1,
+          causal=0, ws=P, wsb=1 << 20):
+        return lib.fa_bwd(q, k, v, o, do, lse, dq, dk, dv, B, Hq, Hkv, Nq, Nk, d, scale, causal, ws, wsb, None)
+    for name in ("q", "k", "v", "o", "do", "lse", "dq", "dk", "dv"):
+        assert f(**{name: None}) == 1, name
+        assert f(**{name: P + 8}) == 4, name
+    assert f(ws=None) == 5
+    assert f(wsb=100) == 5
+    assert f(ws=P + 16) == 4
+    assert f(d=256) == 3
+    assert f(d=96) == 3
+    assert f(Hq=3, Hkv=2) == 2
+    assert f(scale=0.0) == 7
+    assert f(causal=3) == 7
+    assert f(B=0, q=None, k=None, v=None, o=None, do=None, lse=None, dq=None, dk=None, dv=None, ws=None) == 0
 
 
 def test_empty_tensors_may_be_null_but_shapes_still_checked():

@@ -1,0 +1,97 @@
+"""GPU parity of the backward pass (fa_bwd, through the C ABI) against the
+fp64 oracle (oracle.attention_backward) on the same seeded bf16 inputs.
+
+Tolerance, derived from the arithmetic (the task fixes none for gradients):
+every product runs on bf16 operands with fp32 accumulation; P and dS are
+rounded to bf16 (2^-9 relative per term) before dV = P^T dO, dK = dS^T Q and
+dQ = dS K; the outputs are rounded to bf16 (2^-9 relative); D = rowsum(dO O)
+uses the forward's bf16 O, which moves dS by about 2^-9 |dO||O|, small
+against |dP - D|. Sums of such terms keep the relative error near 2^-9 of
+sum |terms|, so per tensor: max |G - G_ref| <= 2e-2 max |G_ref| + 1e-6 and
+||G - G_ref||_F <= 1e-2 ||G_ref||_F (1e-6 per element where G_ref is zero,
+e.g. dQ and dK with a single key, where dS = dP - D vanishes exactly and the
+GPU keeps only fp32 summation-order residue). Rows with no visible key must
+get dQ = 0 exactly."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_helpers import say
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev_bf16(seed, t, shape):
+    import torch
+    bits = synth.draw_bf16(seed, t, shape)
+    return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to("cuda")
+
+
+def _f64(seed, t, shape):
+    return synth.bf16_bits_to_f32(synth.draw_bf16(seed, t, shape)).astype(np.float64)
+
+
+def _run(w):
+    import torch
+    import exact_io_aware_17_amd as fa
+    q, k, v = (_dev_bf16(w.seed, t, s) for t, s in ((0, w.q_shape), (1, w.kv_shape), (2, w.kv_shape)))
+    do = _dev_bf16(w.seed, synth.TENSOR_DO, w.q_shape)
+    say(f"  launch fa_fwd + fa_bwd {w}")
+    o, lse = fa.forward(q, k, v, causal=w.causal, scale=w.scale)
+    dq, dk, dv = fa.backward(q, k, v, o, lse, do, causal=w.causal, scale=w.scale)
+    torch.cuda.synchronize()
+    return [t.float().cpu().numpy().astype(np.float64) for t in (dq, dk, dv)]
+
+
+def _check(got, ref, what):
+    for name, g, r in zip(("dQ", "dK", "dV"), got, ref):
+        assert not np.isnan(g).any(), f"{what} {name}: NaN"
+        scale = float(np.max(np.abs(r))) if r.size else 0.0
+        e_max = float(np.max(np.abs(g - r))) if r.size else 0.0
+        fro = float(np.linalg.norm(g - r) / max(np.linalg.norm(r), 1e-30)) if r.size else 0.0
+        say(f"  {what} {name}: max|d| = {e_max:.3e} ({e_max / max(scale, 1e-30):.2e} of max|ref|), rel-fro {fro:.2e}")
+        assert e_max <= 2e-2 * scale + 1e-6, f"{what} {name}: max error {e_max:.3e} > 2e-2 * {scale:.3e} + 1e-6"
+        if np.linalg.norm(r) > 0:
+            assert fro <= 1e-2, f"{what} {name}: relative Frobenius error {fro:.3e}"
+        else:
+            assert float(np.linalg.norm(g)) <= 1e-6 * np.sqrt(g.size), f"{what} {name}: nonzero gradient"
+
+
+CASES = [
+    synth.Workload("bwd_single_head_n256_d64", 1, 1, 1, 256, 256, 64),
+    synth.Workload("bwd_single_head_n256_d64_causal", 1, 1, 1, 256, 256, 64, causal=True),
+    synth.Workload("bwd_ragged_gqa", 2, 4, 2, 200, 333, 128, seed=1),
+    synth.Workload("bwd_ragged_gqa_causal", 2, 4, 2, 200, 333, 128, causal=True, seed=2),
+    synth.Workload("bwd_more_queries_than_keys_causal", 1, 3, 1, 300, 70, 128, causal=True, seed=5),
+    synth.Workload("bwd_one_query_one_key", 1, 1, 1, 1, 1, 128),
+    synth.Workload("bwd_keys_below_one_block", 1, 2, 2, 150, 17, 128, seed=4),
+    synth.Workload("bwd_gqa_8to1_d64_causal", 1, 8, 1, 130, 190, 64, causal=True, seed=6),
+]
+
+
+@pytest.mark.parametrize("w", CASES, ids=lambda w: w.name)
+def test_bwd_full_oracle(w):
+    say(f"case bwd full {w.name}")
+    got = _run(w)
+    q, k, v = synth.inputs_f64(w)
+    do = _f64(w.seed, synth.TENSOR_DO, w.q_shape)
+    dq, dk, dv, _ = oracle.attention_backward(q, k, v, do, w.scale, w.causal)
+    _check(got, (dq, dk, dv), w.name)
+    if w.causal and w.Nq > w.Nk:
+        assert np.all(got[0][:, :, : w.Nq - w.Nk] == 0.0), "rows without keys must get dQ = 0"
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_full_size_heads(causal):
+    """The batched shape (B4 H16 2048^2 d128) launched in full; the oracle
+    computes two whole heads (MHA: heads are independent)."""
+    w = synth.Workload("bwd_batched_b4h16_n2048", 4, 16, 16, 2048, 2048, 128, causal=causal)
+    say(f"case bwd full-size {w.name} causal={causal}")
+    got = _run(w)
+    for (b, h) in ((0, 0), (3, 15)):
+        q, k, v = synth.inputs_f64(w, q_heads=[(b, h)], kv_heads=[(b, h)])
+        do = synth.bf16_bits_to_f32(synth.draw_bf16(w.seed, synth.TENSOR_DO, w.q_shape, heads=[(b, h)]))
+        do = do.astype(np.float64)
+        dq, dk, dv, _ = oracle.attention_backward(q[:, None], k[:, None], v[:, None], do[:, None], w.scale, causal)
+        _check([g[b:b + 1, h:h + 1] for g in got], (dq, dk, dv), f"{w.name} head ({b},{h})")
