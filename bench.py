@@ -6,11 +6,11 @@ steps; one JSON line on stdout. The line also carries the split-KV decode
 workload (B=64, Hq=32, Hkv=8, Nk=8192, 16 splits) timed the same way, the
 same decode over a paged K/V cache (16-key pages in a random order), the
 pages' shape again with OCP E4M3 inputs through fa_fwd_fp8 and at head
-size 256 through fa_fwd, the
+size 256 through fa_fwd, the backward pass (fa_bwd) on the pages' shape, the
 roofline of the dominant kernel, and the CPU oracle timed on a bounded sample.
 
   python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--all]
-  python bench.py --only prefill|prefill_fp8|prefill_d256|decode|decode_paged --steps 3   (short runs under a profiler)
+  python bench.py --only prefill|prefill_fp8|prefill_d256|backward|decode|decode_paged --steps 3   (short runs under a profiler)
   python bench.py --copy-calib                       (plain copy of known size, for counter scaling)
 """
 from __future__ import annotations
@@ -58,6 +58,7 @@ def kernel_source_sha(files):
 FWD_SOURCES = ["fa_fwd.hip", "fa_common.h"]
 FWD8_SOURCES = ["fa_fwd_fp8.hip", "fa_common.h"]
 FWD256_SOURCES = ["fa_fwd_d256.hip", "fa_common.h"]
+BWD_SOURCES = ["fa_bwd.hip", "fa_common.h"]
 DEC_SOURCES = ["fa_splitkv.hip", "fa_common.h"]
 
 
@@ -138,6 +139,27 @@ def bench_prefill_fp8(w, steps, warmup, device, min_warm_s=0.2):
     wall, ev_ms = time_steps(step, steps, warmup, min_warm_s)
     return {"wall_s": wall, "ms_per_step": wall * 1e3 / steps, "kernel_ms": ev_ms,
             "tflops": w.flops() / (wall / steps) / 1e12, "kernel_tflops": w.flops() / (ev_ms * 1e-3) / 1e12}
+
+
+def bench_backward(w, steps, warmup, device, min_warm_s=0.2):
+    """fa_bwd (prep, main, dQ convert) with O and LSE from one fa_fwd outside
+    the timed steps; dO seeded like the inputs. FLOPs: the five products,
+    2.5 times the forward's."""
+    import torch
+    import exact_io_aware_17_amd as fa
+    q, k, v = device_inputs(w, device)
+    bits = synth.draw_bf16(w.seed, synth.TENSOR_DO, w.q_shape)
+    do = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(device)
+    o, lse = fa.forward(q, k, v, causal=w.causal, scale=w.scale)
+    ws = torch.empty(fa.fa_bwd_workspace_bytes(*w.q_shape), dtype=torch.uint8, device=device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+
+    def step():
+        fa.fa_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, scale=w.scale, causal=w.causal)
+    wall, ev_ms = time_steps(step, steps, warmup, min_warm_s)
+    fl = 2.5 * w.flops()
+    return {"wall_s": wall, "ms_per_step": wall * 1e3 / steps, "kernel_ms": ev_ms,
+            "tflops": fl / (wall / steps) / 1e12, "kernel_tflops": fl / (ev_ms * 1e-3) / 1e12}
 
 
 def bench_decode(w, steps, warmup, device, min_warm_s=0.2):
@@ -256,7 +278,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--all", action="store_true", help="also time the other prefill workloads")
-    ap.add_argument("--only", choices=["prefill", "prefill_fp8", "prefill_d256", "decode", "decode_paged"],
+    ap.add_argument("--only", choices=["prefill", "prefill_fp8", "prefill_d256", "backward", "decode", "decode_paged"],
                     default=None)
     ap.add_argument("--copy-calib", action="store_true")
     args = ap.parse_args()
@@ -281,6 +303,10 @@ def main():
     if args.only == "prefill":
         r = bench_prefill(wp, args.steps, args.warmup, device, min_warm_s=0.0)
         print(json.dumps({"only": "prefill", **r}))
+        return
+    if args.only == "backward":
+        r = bench_backward(wp, args.steps, args.warmup, device, min_warm_s=0.0)
+        print(json.dumps({"only": "backward", **r}))
         return
     if args.only == "prefill_d256":
         r = bench_prefill(synth.WORKLOADS[PREFILL_D256], args.steps, args.warmup, device, min_warm_s=0.0)
@@ -310,6 +336,10 @@ def main():
     log(f"prefill d256 {w256.name}: warmup {args.warmup}, steps {args.steps}")
     r256 = bench_prefill(w256, args.steps, args.warmup, device)
     log(f"  {r256}")
+    bsteps, bwarm = max(1, args.steps // 5), max(1, args.warmup // 5)
+    log(f"backward {wp.name}: warmup {bwarm}, steps {bsteps}")
+    rb = bench_backward(wp, bsteps, bwarm, device)
+    log(f"  {rb}")
     log(f"decode {wd.name}: warmup {args.warmup}, steps {args.steps}")
     rd = bench_decode(wd, args.steps, args.warmup, device)
     log(f"  {rd}")
@@ -330,6 +360,7 @@ def main():
     fwd_traffic = traffic_from_profile("fwd_bf16_pages_shape_traffic.md", FWD_SOURCES)
     fwd8_traffic = traffic_from_profile("fwd_fp8_pages_shape_traffic.md", FWD8_SOURCES)
     fwd256_traffic = traffic_from_profile("fwd_bf16_d256_pages_shape_traffic.md", FWD256_SOURCES)
+    bwd_traffic = traffic_from_profile("bwd_pages_shape_traffic.md", BWD_SOURCES)
     dec_traffic = traffic_from_profile("splitkv_decode_traffic.md", DEC_SOURCES)
     decp_traffic = traffic_from_profile("splitkv_paged_decode_traffic.md", DEC_SOURCES)
     line = {
@@ -367,6 +398,15 @@ def main():
                                       "frac": round(r256["kernel_tflops"] / PEAK_BF16_TFLOPS, 4),
                                       "traffic": fwd256_traffic, "kernel_ms": round(r256["kernel_ms"], 5),
                                       "kernel": "fwd_bf16_d256_kernel<2>"}},
+        "backward": {"workload": wp.name, "dtype": "bf16",
+                     "metric": "attention bwd TFLOPS (2.5 x 4*B*H*Nq*Nk*d: the five products)",
+                     "value": round(rb["tflops"], 2), "unit": "TFLOP/s", "steps": bsteps, "warmup": bwarm,
+                     "ms_per_step": round(rb["ms_per_step"], 5),
+                     "roofline": {"bound": "mfma", "achieved": round(rb["kernel_tflops"], 2),
+                                  "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                                  "frac": round(rb["kernel_tflops"] / PEAK_BF16_TFLOPS, 4), "traffic": bwd_traffic,
+                                  "kernel_ms": round(rb["kernel_ms"], 5),
+                                  "kernel": "bwd_prep_kernel<128> + bwd_main_kernel<128> + bwd_dq_kernel"}},
         "decode": {"workload": wd.name, "metric": "decode HBM GB/s (algorithmic bytes / step time)",
                    "value": round(rd["gbs"], 1), "unit": "GB/s", "ms_per_step": round(rd["ms_per_step"], 5),
                    "roofline": {"bound": "hbm", "achieved": round(rd["kernel_gbs"], 1), "peak": PEAK_HBM_GBS,
