@@ -88,6 +88,31 @@ __device__ __forceinline__ void load_rows(uint16_t* tile, const uint16_t* __rest
   }
 }
 
+// The same copy in two halves: global loads into registers (issued one query
+// block ahead, so their latency hides under the current block's work), then
+// the stores into the LDS tile.
+template <int D>
+struct RowsInFlight {
+  static constexpr int CH = D / 8;
+  static constexpr int N = 64 * CH / kBwdThreads;
+  u32x4 r[N];
+  __device__ __forceinline__ void load(const uint16_t* __restrict__ src, int nrows, int tid) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int id = tid + i * kBwdThreads;
+      const int row = id / CH, ch = id % CH;
+      r[i] = row < nrows ? *reinterpret_cast<const u32x4*>(src + (size_t)row * D + ch * 8) : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  __device__ __forceinline__ void store(uint16_t* tile, int tid) const {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int id = tid + i * kBwdThreads;
+      *reinterpret_cast<u32x4*>(tile + (id / CH) * BwdLayout<D>::RS + (id % CH) * 8) = r[i];
+    }
+  }
+};
+
 template <int D>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO,
                                                        float* __restrict__ Dsum, float* __restrict__ dq_acc,
@@ -157,22 +182,41 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_main_kernel(
     qb0 = first <= 0 ? 0 : (int)(first / kBwdBQ);
   }
   const int n_qb = (Nq + kBwdBQ - 1) / kBwdBQ;
+  // Work items: (query head of the group, query block), query block fastest.
+  const int per_head = n_qb > qb0 ? n_qb - qb0 : 0;
+  const int n_items = group * per_head;
+  RowsInFlight<D> qn, don;
+  float lse_n = kNegInf, d_n = 0.f;
+  auto fetch = [&](int item) __attribute__((always_inline)) {
+    const int hh = item / per_head, qb = qb0 + item % per_head;
+    const size_t bh = (size_t)b * Hq + g * group + hh;
+    const int q0 = qb * kBwdBQ;
+    const int nq = Nq - q0 < kBwdBQ ? Nq - q0 : kBwdBQ;
+    qn.load(Q + (bh * Nq + q0) * D, nq, tid);
+    don.load(dO + (bh * Nq + q0) * D, nq, tid);
+    if (tid < 64) {
+      lse_n = tid < nq ? LSE[bh * Nq + q0 + tid] : kNegInf;
+      d_n = tid < nq ? Dsum[bh * Nq + q0 + tid] : 0.f;
+    }
+  };
+  if (n_items > 0) fetch(0);
 
-  for (int hh = 0; hh < group; ++hh) {
+  for (int item = 0; item < n_items; ++item) {
+    const int hh = item / per_head, qb = qb0 + item % per_head;
     const int h = g * group + hh;
     const size_t bh = (size_t)b * Hq + h;
-    for (int qb = qb0; qb < n_qb; ++qb) {
+    {
       const int q0 = qb * kBwdBQ;
       const int nq = Nq - q0 < kBwdBQ ? Nq - q0 : kBwdBQ;
       __syncthreads();  // the previous block's reads of Qs, dOs, PT, dST are done
-      load_rows<D>(Qs, Q + (bh * Nq + q0) * D, nq, tid);
-      load_rows<D>(dOs, dO + (bh * Nq + q0) * D, nq, tid);
+      qn.store(Qs, tid);
+      don.store(dOs, tid);
       if (tid < 64) {
-        const float l = tid < nq ? LSE[bh * Nq + q0 + tid] : kNegInf;
         // A row without keys (LSE = -inf) or past Nq gets P = 0: exp2(-inf).
-        lse2[tid] = l > kNegInf ? l * kLog2e : __builtin_huge_valf();
-        dsum[tid] = tid < nq ? Dsum[bh * Nq + q0 + tid] : 0.f;
+        lse2[tid] = lse_n > kNegInf ? lse_n * kLog2e : __builtin_huge_valf();
+        dsum[tid] = d_n;
       }
+      if (item + 1 < n_items) fetch(item + 1);
       __syncthreads();
 
       // S and dP, quadrant (query half wq, key half wk) of this wave.
