@@ -10,19 +10,23 @@
 //
 // Kernels:
 //  * bwd_prep_kernel: D_i in fp32 and a zeroed fp32 dQ accumulator (workspace).
-//  * bwd_main_kernel: one workgroup (4 waves) per (batch, KV head, 64-key
+//  * bwd_main_kernel: one workgroup (4 waves) per (batch, KV head, 128-key
 //    block). K and V of the block stay in LDS; the workgroup walks the query
 //    heads of its GQA group and their 64-row query blocks (under the causal
 //    mask only the blocks that see a key of the block). Per query block:
 //      - Q, dO, LSE, D rows into LDS;
-//      - S and dP (64 x 64) with 32x32x16 bf16 MFMAs, one 32 x 32 quadrant
-//        per wave; P = exp2(S scale log2e - LSE log2e), dS = P (dP - D) in
-//        fp32, masked entries 0; P^T and dS^T go to LDS in bf16;
-//      - dV += P^T dO and dK += dS^T Q (64 keys x d) accumulate in
-//        registers, a 32-key x (d/2) block per wave;
-//      - dQ (64 rows x d) = dS K: each wave's 32-row x (d/2) block is added
-//        to the fp32 accumulator with vector atomics (query blocks are shared
-//        by every key block).
+//      - S and dP (64 x 128) with 32x32x16 bf16 MFMAs, a 32-row x 64-key
+//        block per wave; P = exp2(S scale log2e - LSE log2e), dS = P (dP - D)
+//        in fp32, masked entries 0; P^T and dS^T go to LDS in bf16;
+//      - dV += P^T dO and dK += dS^T Q (128 keys x d) accumulate in
+//        registers, a 64-key x (d/2) block per wave;
+//      - dQ (64 rows x d) = dS K over the 128 keys: each wave's 32-row x
+//        (d/2) block is added to the fp32 accumulator with vector atomics
+//        (query blocks are shared by every key block; 128 keys per workgroup
+//        halve these adds, and the per-key cost of each query block, against
+//        64).
+//    The next query block's Q, dO, LSE and D are loaded into registers while
+//    the current one is computed.
 //    Column-wise operands (dO, Q, K and dS read across rows) come from the
 //    transposing LDS read ds_read_b64_tr_b16 (lane semantics in fa_common.h);
 //    rows are padded by 16 bytes so that row-wise 16-byte reads of 16
@@ -36,7 +40,8 @@ namespace {
 
 constexpr int kBwdThreads = 256;
 constexpr int kBwdBQ = 64;  // query rows per block
-constexpr int kBwdBK = 64;  // keys per workgroup
+constexpr int kBwdBK = 128;  // keys per workgroup
+constexpr int kBwdKH = kBwdBK / 64;  // 32-key sub-blocks per wave in the key-side products
 constexpr int kPStride = kBwdBQ + 8;  // P^T / dS^T row stride (elements)
 
 template <int D>
@@ -73,13 +78,13 @@ __device__ __forceinline__ bf16x8 row_operand(const uint16_t* tile, int r0, int 
   return *reinterpret_cast<const bf16x8*>(tile + (r0 + (lane & 31)) * RS + k0 + (lane >> 5) * 8);
 }
 
-// Copy `nrows` valid rows (of 64) of a [rows][D] bf16 tensor into a padded
+// Copy `nrows` valid rows (of ROWS) of a [rows][D] bf16 tensor into a padded
 // LDS tile; missing rows are zero.
-template <int D>
+template <int D, int ROWS>
 __device__ __forceinline__ void load_rows(uint16_t* tile, const uint16_t* __restrict__ src, int nrows, int tid) {
   constexpr int CH = D / 8;  // 16-byte chunks per row
 #pragma unroll
-  for (int i = 0; i < 64 * CH / kBwdThreads; ++i) {
+  for (int i = 0; i < ROWS * CH / kBwdThreads; ++i) {
     const int id = tid + i * kBwdThreads;
     const int row = id / CH, ch = id % CH;
     u32x4 v = u32x4{0u, 0u, 0u, 0u};
@@ -167,12 +172,14 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_main_kernel(
   const uint16_t* Vh = V + ((size_t)(b * Hkv + g) * Nk + k0) * D;
   const int diag = Nk - Nq;
 
-  load_rows<D>(Ks, Kh, nk, tid);
-  load_rows<D>(Vs, Vh, nk, tid);
+  load_rows<D, kBwdBK>(Ks, Kh, nk, tid);
+  load_rows<D, kBwdBK>(Vs, Vh, nk, tid);
 
-  f32x16 dv[L::DB], dk[L::DB];
+  f32x16 dv[kBwdKH][L::DB], dk[kBwdKH][L::DB];
 #pragma unroll
-  for (int i = 0; i < L::DB; ++i) dv[i] = dk[i] = f32x16{};
+  for (int kk = 0; kk < kBwdKH; ++kk)
+#pragma unroll
+    for (int i = 0; i < L::DB; ++i) dv[kk][i] = dk[kk][i] = f32x16{};
 
   // Query blocks that see a key of this block: under the causal mask, row i
   // sees key j iff j <= i + diag, so rows below k0 - diag see none.
@@ -219,16 +226,19 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_main_kernel(
       if (item + 1 < n_items) fetch(item + 1);
       __syncthreads();
 
-      // S and dP, quadrant (query half wq, key half wk) of this wave.
+      // S and dP: query half wq, keys wk*64 + 32 kk (kk = 0, 1) of this wave.
       const int wq = wave >> 1, wk = wave & 1;
+#pragma unroll
+      for (int kk = 0; kk < kBwdKH; ++kk) {
+      const int kr0 = wk * 64 + kk * 32;
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        s = mfma32(row_operand<RS>(Qs, wq * 32, ks * 16, lane), row_operand<RS>(Ks, wk * 32, ks * 16, lane), s);
-        dp = mfma32(row_operand<RS>(dOs, wq * 32, ks * 16, lane), row_operand<RS>(Vs, wk * 32, ks * 16, lane), dp);
+        s = mfma32(row_operand<RS>(Qs, wq * 32, ks * 16, lane), row_operand<RS>(Ks, kr0, ks * 16, lane), s);
+        dp = mfma32(row_operand<RS>(dOs, wq * 32, ks * 16, lane), row_operand<RS>(Vs, kr0, ks * 16, lane), dp);
       }
-      // C layout: lane l holds key wk*32 + l%32, query rows wq*32 + (i/4)*8 + 4 hl + i%4.
-      const int kl = wk * 32 + (lane & 31);
+      // C layout: lane l holds key kr0 + l%32, query rows wq*32 + (i/4)*8 + 4 hl + i%4.
+      const int kl = kr0 + (lane & 31);
       const int key = k0 + kl;
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
@@ -252,21 +262,31 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_main_kernel(
         *reinterpret_cast<u32x2*>(PT + kl * kPStride + ql) = u32x2{pw[0], pw[1]};
         *reinterpret_cast<u32x2*>(dST + kl * kPStride + ql) = u32x2{dw[0], dw[1]};
       }
+      }
       __syncthreads();
 
-      // dV += P^T dO and dK += dS^T Q: keys half*32.., d blocks dh*(D/2) + 32 i.
+      // dV += P^T dO and dK += dS^T Q: keys half*64 + 32 kk, d blocks dh*(D/2) + 32 i.
 #pragma unroll
       for (int ks = 0; ks < kBwdBQ / 16; ++ks) {
-        const bf16x8 ap = row_operand<kPStride>(PT, half * 32, ks * 16, lane);
-        const bf16x8 as = row_operand<kPStride>(dST, half * 32, ks * 16, lane);
+        bf16x8 bo[L::DB], bq[L::DB];
 #pragma unroll
         for (int i = 0; i < L::DB; ++i) {
           const int c0 = dh * (D / 2) + i * 32;
-          dv[i] = mfma32(ap, col_operand<RS>(dOs, ks * 16, c0, lane), dv[i]);
-          dk[i] = mfma32(as, col_operand<RS>(Qs, ks * 16, c0, lane), dk[i]);
+          bo[i] = col_operand<RS>(dOs, ks * 16, c0, lane);
+          bq[i] = col_operand<RS>(Qs, ks * 16, c0, lane);
+        }
+#pragma unroll
+        for (int kk = 0; kk < kBwdKH; ++kk) {
+          const bf16x8 ap = row_operand<kPStride>(PT, half * 64 + kk * 32, ks * 16, lane);
+          const bf16x8 as = row_operand<kPStride>(dST, half * 64 + kk * 32, ks * 16, lane);
+#pragma unroll
+          for (int i = 0; i < L::DB; ++i) {
+            dv[kk][i] = mfma32(ap, bo[i], dv[kk][i]);
+            dk[kk][i] = mfma32(as, bq[i], dk[kk][i]);
+          }
         }
       }
-      // dQ rows half*32.. (+ q0), d blocks dh*(D/2) + 32 i: dS K over the 64 keys.
+      // dQ rows half*32.. (+ q0), d blocks dh*(D/2) + 32 i: dS K over the 128 keys.
       f32x16 dq[L::DB];
 #pragma unroll
       for (int i = 0; i < L::DB; ++i) dq[i] = f32x16{};
@@ -291,15 +311,17 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_main_kernel(
 
   // dK (times scale) and dV, bf16: lane holds d column, key rows (i/4)*8 + 4 hl + i%4.
 #pragma unroll
+  for (int kk = 0; kk < kBwdKH; ++kk)
+#pragma unroll
   for (int i = 0; i < L::DB; ++i) {
     const int d = dh * (D / 2) + i * 32 + (lane & 31);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int kl = half * 32 + (r >> 2) * 8 + hl * 4 + (r & 3);
+      const int kl = half * 64 + kk * 32 + (r >> 2) * 8 + hl * 4 + (r & 3);
       if (kl < nk) {
         const size_t off = ((size_t)(b * Hkv + g) * Nk + k0 + kl) * D + d;
-        dK[off] = __builtin_bit_cast(uint16_t, (__bf16)(dk[i][r] * scale));
-        dV[off] = __builtin_bit_cast(uint16_t, (__bf16)dv[i][r]);
+        dK[off] = __builtin_bit_cast(uint16_t, (__bf16)(dk[kk][i][r] * scale));
+        dV[off] = __builtin_bit_cast(uint16_t, (__bf16)dv[kk][i][r]);
       }
     }
   }
