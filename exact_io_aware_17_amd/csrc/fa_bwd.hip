@@ -162,8 +162,13 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_main_kernel(
   const int hl = lane >> 5;
   const int half = wave & 1, dh = wave >> 1;  // quadrant / block owned by this wave
 
-  const int kb = blockIdx.x % n_kb;
-  const int bg = blockIdx.x / n_kb;
+  // Key-block-major order: under the causal mask the first key blocks see the
+  // most query blocks, so the longest workgroups start first; with B * Hkv a
+  // multiple of 8 all key blocks of a head also land on one XCD (shared L2
+  // for that head's Q and dO).
+  const int n_bg = gridDim.x / n_kb;
+  const int kb = blockIdx.x / n_bg;
+  const int bg = blockIdx.x - kb * n_bg;
   const int b = bg / Hkv, g = bg - b * Hkv;
   const int group = Hq / Hkv;
   const int k0 = kb * kBwdBK;
