@@ -82,14 +82,20 @@ def test_bwd_full_oracle(w):
         assert np.all(got[0][:, :, : w.Nq - w.Nk] == 0.0), "rows without keys must get dQ = 0"
 
 
-@pytest.mark.parametrize("causal", [False, True])
-def test_bwd_full_size_heads(causal):
-    """The batched shape (B4 H16 2048^2 d128) launched in full; the oracle
-    computes two whole heads (MHA: heads are independent)."""
-    w = synth.Workload("bwd_batched_b4h16_n2048", 4, 16, 16, 2048, 2048, 128, causal=causal)
+@pytest.mark.parametrize("name", ["batched", "batched_causal", "pages_shape"])
+def test_bwd_full_size_heads(name):
+    """Full-size launches: the batched shape (B4 H16 2048^2 d128), with and
+    without causal, and the pages' shape (B1 H8 4096 x 8192, the benchmark's
+    backward); the oracle computes two whole heads (MHA: heads are
+    independent)."""
+    if name == "pages_shape":
+        w = synth.WORKLOADS["pages_shape_h8_q4096_kv8192"]
+    else:
+        w = synth.Workload("bwd_batched_b4h16_n2048", 4, 16, 16, 2048, 2048, 128, causal=name.endswith("causal"))
+    causal = w.causal
     say(f"case bwd full-size {w.name} causal={causal}")
     got = _run(w)
-    for (b, h) in ((0, 0), (3, 15)):
+    for (b, h) in ((0, 0), (w.B - 1, w.Hq - 1)):
         q, k, v = synth.inputs_f64(w, q_heads=[(b, h)], kv_heads=[(b, h)])
         do = synth.bf16_bits_to_f32(synth.draw_bf16(w.seed, synth.TENSOR_DO, w.q_shape, heads=[(b, h)]))
         do = do.astype(np.float64)

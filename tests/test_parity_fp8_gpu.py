@@ -112,6 +112,25 @@ def test_fp8_pages_shape_full_size_sampled():
         _check(o[:, h:h + 1, rows], lse[:, h:h + 1, rows], o_ref, lse_ref, bound, f"{w.name} head {h}")
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_large_shapes_sampled(causal):
+    """The largest fp8 launches: B4 H16 2048^2 and, causal, B1 H32 16384^2;
+    sampled rows of two heads against the oracle."""
+    w = (synth.Workload("fp8_long_causal_h32_n16384", 1, 32, 32, 16384, 16384, 128, causal=True) if causal
+         else synth.Workload("fp8_batched_b4h16_n2048", 4, 16, 16, 2048, 2048, 128))
+    say(f"case fp8 full-size {w.name}")
+    q8, k8, v8 = _inputs(w)
+    o, lse = _run(q8, k8, v8, w.scale, w.causal)
+    rows = sample_rows(w.Nq)
+    for (b, h) in ((0, 0), (w.B - 1, w.Hq - 1)):
+        q = oracle.e4m3_decode(q8[b:b + 1, h:h + 1, rows]) * DS[0]
+        k = oracle.e4m3_decode(k8[b:b + 1, h:h + 1]) * DS[1]
+        v = oracle.e4m3_decode(v8[b:b + 1, h:h + 1]) * DS[2]
+        o_ref, lse_ref = oracle.attention(q, k, v, w.scale, w.causal, q_index=rows, nq=w.Nq)
+        bound = _bound(q, k, v, w.scale, w.causal, o_ref, q_index=rows, nq=w.Nq)
+        _check(o[b:b + 1, h:h + 1, rows], lse[b:b + 1, h:h + 1, rows], o_ref, lse_ref, bound, f"{w.name} ({b},{h})")
+
+
 def test_fp8_identical_keys_exact_probabilities():
     """Every key equal: every probability is the same power of two, so P is
     exact in E4M3 and O is the column mean of V (bf16 output rounding only);
