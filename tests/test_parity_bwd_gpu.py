@@ -101,3 +101,20 @@ def test_bwd_full_size_heads(name):
         do = do.astype(np.float64)
         dq, dk, dv, _ = oracle.attention_backward(q[:, None], k[:, None], v[:, None], do[:, None], w.scale, causal)
         _check([g[b:b + 1, h:h + 1] for g in got], (dq, dk, dv), f"{w.name} head ({b},{h})")
+
+
+def test_bwd_degenerate_sizes():
+    """Nq = 0: no query, so dK = dV = 0; Nk = 0: no key, so dQ = 0 (the
+    forward gives O = 0 and LSE = -inf)."""
+    import torch
+    import exact_io_aware_17_amd as fa
+    for (nq, nk) in ((0, 70), (50, 0)):
+        w = synth.Workload(f"bwd_degenerate_{nq}_{nk}", 1, 2, 1, nq, nk, 128, causal=True)
+        say(f"case bwd degenerate Nq={nq} Nk={nk}")
+        q, k, v = (_dev_bf16(w.seed, t, s) for t, s in ((0, w.q_shape), (1, w.kv_shape), (2, w.kv_shape)))
+        do = _dev_bf16(w.seed, synth.TENSOR_DO, w.q_shape)
+        o, lse = fa.forward(q, k, v, causal=True, scale=w.scale)
+        dq, dk, dv = fa.backward(q, k, v, o, lse, do, causal=True, scale=w.scale)
+        torch.cuda.synchronize()
+        for t in (dq, dk, dv):
+            assert t.numel() == 0 or float(t.float().abs().max()) == 0.0

@@ -213,3 +213,15 @@ def test_fp8_argument_errors():
     z = torch.zeros((0, 2, 8, 128), dtype=torch.uint8, device="cuda")
     fa.fa_fwd_fp8(z, z, z, torch.empty((0, 2, 8, 128), dtype=torch.bfloat16, device="cuda"),
                   torch.empty((0, 2, 8), dtype=torch.float32, device="cuda"), DS)
+
+
+def test_fp8_no_keys_and_no_queries():
+    """Nk = 0: every row has no key (O = 0, LSE = -inf); Nq = 0: nothing to do."""
+    w = synth.Workload("fp8_no_keys", 1, 2, 1, 40, 0, 128)
+    q8, k8, v8 = _inputs(w)
+    o, lse = _run(q8, k8, v8, w.scale, False)
+    assert np.all(o == 0.0) and np.all(np.isneginf(lse))
+    w = synth.Workload("fp8_no_queries", 1, 2, 1, 0, 40, 128)
+    q8, k8, v8 = _inputs(w)
+    o, lse = _run(q8, k8, v8, w.scale, False)
+    assert o.size == 0 and lse.size == 0
