@@ -11,20 +11,24 @@
 // Kernels:
 //  * bwd_prep_kernel: D_i in fp32 and a zeroed fp32 dQ accumulator (workspace).
 //  * bwd_main_kernel: one workgroup (4 waves) per (batch, KV head, 128-key
-//    block). K and V of the block stay in LDS; the workgroup walks the query
-//    heads of its GQA group and their 64-row query blocks (under the causal
-//    mask only the blocks that see a key of the block). Per query block:
+//    block); each wave owns 32 keys of the block. Their K and V rows stay in
+//    registers as the B operands of S = Q K^T and dP = dO V^T, and K also
+//    sits in LDS for dQ. The workgroup walks the query heads of its GQA
+//    group and their 64-row query blocks (under the causal mask only the
+//    blocks that see a key of the block). Per query block:
 //      - Q, dO, LSE, D rows into LDS;
-//      - S and dP (64 x 128) with 32x32x16 bf16 MFMAs, a 32-row x 64-key
-//        block per wave; P = exp2(S scale log2e - LSE log2e), dS = P (dP - D)
-//        in fp32, masked entries 0; P^T and dS^T go to LDS in bf16;
-//      - dV += P^T dO and dK += dS^T Q (128 keys x d) accumulate in
-//        registers, a 64-key x (d/2) block per wave;
-//      - dQ (64 rows x d) = dS K over the 128 keys: each wave's 32-row x
-//        (d/2) block is added to the fp32 accumulator with vector atomics
-//        (query blocks are shared by every key block; 128 keys per workgroup
-//        halve these adds, and the per-key cost of each query block, against
-//        64).
+//      - S and dP (64 rows x the wave's 32 keys) with 32x32x16 bf16 MFMAs;
+//        P = exp2(S scale log2e - LSE log2e), dS = P (dP - D) in fp32,
+//        masked entries 0 (masks only where a ragged or diagonal block
+//        needs them);
+//      - P and dS stay in registers: in the MFMA result each lane holds one
+//        key and 16 rows, which is the A operand of dV += P^T dO and
+//        dK += dS^T Q once dO and Q are read in that row order; dK and dV
+//        (32 keys x d per wave) accumulate in registers;
+//      - dS^T goes to LDS, and dQ (64 rows x d) = dS K over the 128 keys is
+//        added, a 32-row x (d/2) block per wave, to the fp32 accumulator
+//        with vector atomics (query blocks are shared by every key block;
+//        128 keys per workgroup halve these adds against 64).
 //    The next query block's Q, dO, LSE and D are loaded into registers while
 //    the current one is computed.
 //    Column-wise operands (dO, Q, K and dS read across rows) come from the
@@ -32,6 +36,8 @@
 //    rows are padded by 16 bytes so that row-wise 16-byte reads of 16
 //    consecutive rows touch distinct banks.
 //  * bwd_dq_kernel: dQ accumulator -> bf16.
+#include <type_traits>
+
 #include "fa_common.h"
 #include "fa_internal.h"
 
@@ -46,15 +52,15 @@ constexpr int kPStride = kBwdBQ + 8;  // P^T / dS^T row stride (elements)
 
 template <int D>
 struct BwdLayout {
-  static constexpr int RS = D + 8;  // row stride of K, V, Q, dO tiles (elements)
+  static constexpr int RS = D + 8;  // row stride of the K, Q and dO tiles (elements)
   static constexpr int K_OFF = 0;
-  static constexpr int V_OFF = K_OFF + kBwdBK * RS;
-  static constexpr int Q_OFF = V_OFF + kBwdBK * RS;
+  static constexpr int Q_OFF = K_OFF + kBwdBK * RS;
   static constexpr int DO_OFF = Q_OFF + kBwdBQ * RS;
-  static constexpr int PT_OFF = DO_OFF + kBwdBQ * RS;
-  static constexpr int DST_OFF = PT_OFF + kBwdBK * kPStride;
+  static constexpr int DST_OFF = DO_OFF + kBwdBQ * RS;
   static constexpr int ELEMS = DST_OFF + kBwdBK * kPStride;  // bf16 elements; then 2 x 64 floats
-  static constexpr int DB = D / 64;  // 32-wide d blocks per wave (each wave owns half of d)
+  static constexpr int KS = D / 16;  // 16-wide d steps of S and dP
+  static constexpr int DT = D / 32;  // 32-wide d tiles of dK and dV (each wave: all of d)
+  static constexpr int DB = D / 64;  // 32-wide d tiles of dQ per wave (each wave: half of d)
 };
 
 // Operand of a 32x32x16 MFMA read across rows of a row-major bf16 tile
@@ -68,6 +74,23 @@ __device__ __forceinline__ bf16x8 col_operand(const uint16_t* tile, int r0, int 
   const int col = c0 + (grp & 1) * 16 + j * 4;
   const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(tile + row * RS + col));
   const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(tile + (row + 4) * RS + col));
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// The same read for a B operand that pairs with an A operand taken straight
+// from a 32x32 MFMA result. In that result lane l holds rows
+// 8 (i / 4) + 4 (l / 32) + i % 4 (i = 0..15) of column l % 32, so elements
+// 0..7 of lane l are rows 4 (l / 32) + 0..3 and 8 + 4 (l / 32) + 0..3 (and
+// elements 8..15 the same rows + 16). Lane l gets column c0 + l % 32 of rows
+// r0 + 4 (l / 32) + 0..3 and r0 + 8 + 4 (l / 32) + 0..3: the k index of the
+// product runs over those rows in the result's order.
+template <int RS>
+__device__ __forceinline__ bf16x8 col_operand_c(const uint16_t* tile, int r0, int c0, int lane) {
+  const int grp = lane >> 4, w = lane & 15, e = w >> 2, j = w & 3;
+  const int row = r0 + (lane >> 5) * 4 + e;
+  const int col = c0 + (grp & 1) * 16 + j * 4;
+  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(tile + row * RS + col));
+  const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(tile + (row + 8) * RS + col));
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
@@ -102,6 +125,14 @@ struct RowsInFlight {
   static constexpr int N = 64 * CH / kBwdThreads;
   u32x4 r[N];
   __device__ __forceinline__ void load(const uint16_t* __restrict__ src, int nrows, int tid) {
+    if (nrows == 64) {
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        const int id = tid + i * kBwdThreads;
+        r[i] = *reinterpret_cast<const u32x4*>(src + (size_t)(id / CH) * D + (id % CH) * 8);
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       const int id = tid + i * kBwdThreads;
@@ -145,14 +176,11 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_main_kernel(
     float* __restrict__ dq_acc, uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int Hq, int Hkv, int Nq,
     int Nk, float scale, float sl2, int causal, int n_kb) {
   using L = BwdLayout<D>;
-  constexpr int RS = L::RS;
-  constexpr int KS = D / 16;
+  constexpr int RS = L::RS, KS = L::KS, DT = L::DT;
   __shared__ __attribute__((aligned(16))) uint16_t lds[L::ELEMS + 2 * 64 * 2];
   uint16_t* Ks = lds + L::K_OFF;
-  uint16_t* Vs = lds + L::V_OFF;
   uint16_t* Qs = lds + L::Q_OFF;
   uint16_t* dOs = lds + L::DO_OFF;
-  uint16_t* PT = lds + L::PT_OFF;
   uint16_t* dST = lds + L::DST_OFF;
   float* lse2 = reinterpret_cast<float*>(lds + L::ELEMS);
   float* dsum = lse2 + 64;
@@ -160,7 +188,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_main_kernel(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hl = lane >> 5;
-  const int half = wave & 1, dh = wave >> 1;  // quadrant / block owned by this wave
+  const int half = wave & 1, dh = wave >> 1;  // dQ block owned by this wave
 
   // Key-block-major order: under the causal mask the first key blocks see the
   // most query blocks, so the longest workgroups start first; with B * Hkv a
@@ -177,14 +205,24 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_main_kernel(
   const uint16_t* Vh = V + ((size_t)(b * Hkv + g) * Nk + k0) * D;
   const int diag = Nk - Nq;
 
+  // K in LDS for dQ = dS K. Each wave owns 32 keys of the block for S, dP, dK
+  // and dV: their K and V rows stay in registers as the B operands of
+  // S = Q K^T and dP = dO V^T (lane l: key wave*32 + l%32, d = 16 ks + 8 (l/32) + 0..7).
   load_rows<D, kBwdBK>(Ks, Kh, nk, tid);
-  load_rows<D, kBwdBK>(Vs, Vh, nk, tid);
+  const int kw = wave * 32 + (lane & 31);
+  bf16x8 kop[KS], vop[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    kop[ks] = vop[ks] = bf16x8{};
+    if (kw < nk) {
+      kop[ks] = *reinterpret_cast<const bf16x8*>(Kh + (size_t)kw * D + ks * 16 + hl * 8);
+      vop[ks] = *reinterpret_cast<const bf16x8*>(Vh + (size_t)kw * D + ks * 16 + hl * 8);
+    }
+  }
 
-  f32x16 dv[kBwdKH][L::DB], dk[kBwdKH][L::DB];
+  f32x16 dv[DT], dk[DT];
 #pragma unroll
-  for (int kk = 0; kk < kBwdKH; ++kk)
-#pragma unroll
-    for (int i = 0; i < L::DB; ++i) dv[kk][i] = dk[kk][i] = f32x16{};
+  for (int i = 0; i < DT; ++i) dv[i] = dk[i] = f32x16{};
 
   // Query blocks that see a key of this block: under the causal mask, row i
   // sees key j iff j <= i + diag, so rows below k0 - diag see none.
@@ -213,120 +251,134 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_main_kernel(
   };
   if (n_items > 0) fetch(0);
 
+  const int key = k0 + kw;
   for (int item = 0; item < n_items; ++item) {
     const int hh = item / per_head, qb = qb0 + item % per_head;
     const int h = g * group + hh;
     const size_t bh = (size_t)b * Hq + h;
-    {
-      const int q0 = qb * kBwdBQ;
-      const int nq = Nq - q0 < kBwdBQ ? Nq - q0 : kBwdBQ;
-      __syncthreads();  // the previous block's reads of Qs, dOs, PT, dST are done
-      qn.store(Qs, tid);
-      don.store(dOs, tid);
-      if (tid < 64) {
-        // A row without keys (LSE = -inf) or past Nq gets P = 0: exp2(-inf).
-        lse2[tid] = lse_n > kNegInf ? lse_n * kLog2e : __builtin_huge_valf();
-        dsum[tid] = d_n;
-      }
-      if (item + 1 < n_items) fetch(item + 1);
-      __syncthreads();
+    const int q0 = qb * kBwdBQ;
+    const int nq = Nq - q0 < kBwdBQ ? Nq - q0 : kBwdBQ;
+    __syncthreads();  // the previous block's reads of Qs, dOs and dST are done
+    qn.store(Qs, tid);
+    don.store(dOs, tid);
+    if (tid < 64) {
+      // A row without keys (LSE = -inf) or past Nq gets P = 0: exp2(-inf).
+      lse2[tid] = lse_n > kNegInf ? lse_n * kLog2e : __builtin_huge_valf();
+      dsum[tid] = d_n;
+    }
+    if (item + 1 < n_items) fetch(item + 1);
+    __syncthreads();
 
-      // S and dP: query half wq, keys wk*64 + 32 kk (kk = 0, 1) of this wave.
-      const int wq = wave >> 1, wk = wave & 1;
+    // S and dP for the 64 rows (two 32-row tiles) x this wave's 32 keys.
+    f32x16 s[2], dp[2];
 #pragma unroll
-      for (int kk = 0; kk < kBwdKH; ++kk) {
-      const int kr0 = wk * 64 + kk * 32;
-      f32x16 s = f32x16{}, dp = f32x16{};
+    for (int qt = 0; qt < 2; ++qt) s[qt] = dp[qt] = f32x16{};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        s = mfma32(row_operand<RS>(Qs, wq * 32, ks * 16, lane), row_operand<RS>(Ks, kr0, ks * 16, lane), s);
-        dp = mfma32(row_operand<RS>(dOs, wq * 32, ks * 16, lane), row_operand<RS>(Vs, kr0, ks * 16, lane), dp);
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        s[qt] = mfma32(row_operand<RS>(Qs, qt * 32, ks * 16, lane), kop[ks], s[qt]);
+        dp[qt] = mfma32(row_operand<RS>(dOs, qt * 32, ks * 16, lane), vop[ks], dp[qt]);
       }
-      // C layout: lane l holds key kr0 + l%32, query rows wq*32 + (i/4)*8 + 4 hl + i%4.
-      const int kl = kr0 + (lane & 31);
-      const int key = k0 + kl;
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const int ql = wq * 32 + i4 * 8 + hl * 4;
-        uint32_t pw[2], dw[2];
-#pragma unroll
-        for (int j = 0; j < 4; j += 2) {
-          float pv[2], dv2[2];
-#pragma unroll
-          for (int jj = 0; jj < 2; ++jj) {
-            const int i = i4 * 4 + j + jj;
-            const int qr = ql + j + jj;
-            const bool vis = key < Nk && (!causal || key <= q0 + qr + diag);
-            const float p = vis ? fast_exp2(__builtin_fmaf(s[i], sl2, -lse2[qr])) : 0.f;
-            pv[jj] = p;
-            dv2[jj] = p * (dp[i] - dsum[qr]);
-          }
-          pw[j >> 1] = pack_bf16x2(pv[0], pv[1]);
-          dw[j >> 1] = pack_bf16x2(dv2[0], dv2[1]);
-        }
-        *reinterpret_cast<u32x2*>(PT + kl * kPStride + ql) = u32x2{pw[0], pw[1]};
-        *reinterpret_cast<u32x2*>(dST + kl * kPStride + ql) = u32x2{dw[0], dw[1]};
-      }
-      }
-      __syncthreads();
 
-      // dV += P^T dO and dK += dS^T Q: keys half*64 + 32 kk, d blocks dh*(D/2) + 32 i.
+    // P and dS. C layout: lane l holds key kw, rows qt*32 + 8 (i/4) + 4 hl + i%4.
+    // Elements 8 h2 + 0..7 of a tile are the A operand (k = those rows) of one
+    // 16-row step of dV += P^T dO and dK += dS^T Q; dS^T also goes to LDS for dQ.
+    u32x4 pa[2][2], da[2][2];
+    // Masks are needed only at a ragged key block or where the causal
+    // diagonal crosses the block (row 0 of the block sees its last key
+    // otherwise); rows past Nq have P = 0 through their LSE either way.
+    const bool full = nk == kBwdBK && (!causal || k0 + kBwdBK - 1 <= q0 + diag);
+    auto p_ds = [&](auto masked) __attribute__((always_inline)) {
 #pragma unroll
-      for (int ks = 0; ks < kBwdBQ / 16; ++ks) {
-        bf16x8 bo[L::DB], bq[L::DB];
+      for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
-        for (int i = 0; i < L::DB; ++i) {
-          const int c0 = dh * (D / 2) + i * 32;
-          bo[i] = col_operand<RS>(dOs, ks * 16, c0, lane);
-          bq[i] = col_operand<RS>(Qs, ks * 16, c0, lane);
-        }
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int ql = qt * 32 + i4 * 8 + hl * 4;
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2 + ql);
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(dsum + ql);
+          float pv[4], dsv[4];
 #pragma unroll
-        for (int kk = 0; kk < kBwdKH; ++kk) {
-          const bf16x8 ap = row_operand<kPStride>(PT, half * 64 + kk * 32, ks * 16, lane);
-          const bf16x8 as = row_operand<kPStride>(dST, half * 64 + kk * 32, ks * 16, lane);
-#pragma unroll
-          for (int i = 0; i < L::DB; ++i) {
-            dv[kk][i] = mfma32(ap, bo[i], dv[kk][i]);
-            dk[kk][i] = mfma32(as, bq[i], dk[kk][i]);
+          for (int j = 0; j < 4; ++j) {
+            const int i = i4 * 4 + j;
+            float p = fast_exp2(__builtin_fmaf(s[qt][i], sl2, -l4[j]));
+            if (decltype(masked)::value) {
+              const bool vis = key < Nk && (!causal || key <= q0 + ql + j + diag);
+              p = vis ? p : 0.f;
+            }
+            pv[j] = p;
+            dsv[j] = p * (dp[qt][i] - d4[j]);
           }
+          const uint32_t p0 = pack_bf16x2(pv[0], pv[1]), p1 = pack_bf16x2(pv[2], pv[3]);
+          const uint32_t d0 = pack_bf16x2(dsv[0], dsv[1]), d1 = pack_bf16x2(dsv[2], dsv[3]);
+          pa[qt][i4 >> 1][(i4 & 1) * 2] = p0;
+          pa[qt][i4 >> 1][(i4 & 1) * 2 + 1] = p1;
+          da[qt][i4 >> 1][(i4 & 1) * 2] = d0;
+          da[qt][i4 >> 1][(i4 & 1) * 2 + 1] = d1;
+          *reinterpret_cast<u32x2*>(dST + kw * kPStride + ql) = u32x2{d0, d1};
+        }
+    };
+    if (full)
+      p_ds(std::false_type{});
+    else
+      p_ds(std::true_type{});
+
+    // dV += P^T dO and dK += dS^T Q: this wave's 32 keys x all of d, B operands
+    // read in the row order of the A operands.
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const bf16x8 ap = __builtin_bit_cast(bf16x8, pa[qt][h2]);
+        const bf16x8 as = __builtin_bit_cast(bf16x8, da[qt][h2]);
+        const int r0 = qt * 32 + h2 * 16;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          dv[dt] = mfma32(ap, col_operand_c<RS>(dOs, r0, dt * 32, lane), dv[dt]);
+          dk[dt] = mfma32(as, col_operand_c<RS>(Qs, r0, dt * 32, lane), dk[dt]);
         }
       }
-      // dQ rows half*32.. (+ q0), d blocks dh*(D/2) + 32 i: dS K over the 128 keys.
-      f32x16 dq[L::DB];
+    __syncthreads();  // dS^T of all 128 keys is in LDS
+
+    // dQ rows half*32.. (+ q0), d blocks dh*(D/2) + 32 i: dS K over the 128 keys.
+    f32x16 dq[L::DB];
 #pragma unroll
-      for (int i = 0; i < L::DB; ++i) dq[i] = f32x16{};
+    for (int i = 0; i < L::DB; ++i) dq[i] = f32x16{};
 #pragma unroll
-      for (int ks = 0; ks < kBwdBK / 16; ++ks) {
-        const bf16x8 a = col_operand<kPStride>(dST, ks * 16, half * 32, lane);
+    for (int ks = 0; ks < kBwdBK / 16; ++ks) {
+      const bf16x8 a = col_operand<kPStride>(dST, ks * 16, half * 32, lane);
 #pragma unroll
-        for (int i = 0; i < L::DB; ++i) dq[i] = mfma32(a, col_operand<RS>(Ks, ks * 16, dh * (D / 2) + i * 32, lane), dq[i]);
-      }
-      // C layout: lane l holds d column c0 + l%32, rows (i/4)*8 + 4 hl + i%4.
+      for (int i = 0; i < L::DB; ++i) dq[i] = mfma32(a, col_operand<RS>(Ks, ks * 16, dh * (D / 2) + i * 32, lane), dq[i]);
+    }
+    // C layout: lane l holds d column c0 + l%32, rows (i/4)*8 + 4 hl + i%4.
+    float* dq_row = dq_acc + (bh * Nq + q0 + half * 32 + hl * 4) * D + dh * (D / 2) + (lane & 31);
+    if (nq == kBwdBQ) {
 #pragma unroll
-      for (int i = 0; i < L::DB; ++i) {
-        const int d = dh * (D / 2) + i * 32 + (lane & 31);
+      for (int i = 0; i < L::DB; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) unsafeAtomicAdd(dq_row + ((r >> 2) * 8 + (r & 3)) * D + i * 32, dq[i][r] * scale);
+    } else {
+#pragma unroll
+      for (int i = 0; i < L::DB; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int ql = half * 32 + (r >> 2) * 8 + hl * 4 + (r & 3);
-          if (ql < nq) unsafeAtomicAdd(dq_acc + (bh * Nq + q0 + ql) * D + d, dq[i][r] * scale);
+          if (ql < nq) unsafeAtomicAdd(dq_row + ((r >> 2) * 8 + (r & 3)) * D + i * 32, dq[i][r] * scale);
         }
-      }
     }
   }
 
-  // dK (times scale) and dV, bf16: lane holds d column, key rows (i/4)*8 + 4 hl + i%4.
+  // dK (times scale) and dV, bf16: lane holds d column, key rows wave*32 + (i/4)*8 + 4 hl + i%4.
 #pragma unroll
-  for (int kk = 0; kk < kBwdKH; ++kk)
-#pragma unroll
-  for (int i = 0; i < L::DB; ++i) {
-    const int d = dh * (D / 2) + i * 32 + (lane & 31);
+  for (int dt = 0; dt < DT; ++dt) {
+    const int d = dt * 32 + (lane & 31);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int kl = half * 64 + kk * 32 + (r >> 2) * 8 + hl * 4 + (r & 3);
+      const int kl = wave * 32 + (r >> 2) * 8 + hl * 4 + (r & 3);
       if (kl < nk) {
         const size_t off = ((size_t)(b * Hkv + g) * Nk + k0 + kl) * D + d;
-        dK[off] = __builtin_bit_cast(uint16_t, (__bf16)(dk[kk][i][r] * scale));
-        dV[off] = __builtin_bit_cast(uint16_t, (__bf16)dv[kk][i][r]);
+        dK[off] = __builtin_bit_cast(uint16_t, (__bf16)(dk[dt][r] * scale));
+        dV[off] = __builtin_bit_cast(uint16_t, (__bf16)dv[dt][r]);
       }
     }
   }
