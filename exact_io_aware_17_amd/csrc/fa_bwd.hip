@@ -30,7 +30,9 @@
 //        with vector atomics (query blocks are shared by every key block;
 //        128 keys per workgroup halve these adds against 64).
 //    The next query block's Q, dO, LSE and D are loaded into registers while
-//    the current one is computed.
+//    the current one is computed, and stored to LDS before the current dQ
+//    adds are issued (the wait for a load also waits for every earlier
+//    atomic of the wave).
 //    Column-wise operands (dO, Q, K and dS read across rows) come from the
 //    transposing LDS read ds_read_b64_tr_b16 (lane semantics in fa_common.h);
 //    rows are padded by 16 bytes so that row-wise 16-byte reads of 16
@@ -219,6 +221,10 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_main_kernel(
       vop[ks] = *reinterpret_cast<const bf16x8*>(Vh + (size_t)kw * D + ks * 16 + hl * 8);
     }
   }
+  // Retire these loads here (vmcnt 0; expcnt and lgkmcnt left alone): left
+  // pending into the loop, the per-register wait tracking would make the
+  // first MFMA of every query block wait for that block's prefetch loads too.
+  __builtin_amdgcn_s_waitcnt(0x0F70);
 
   f32x16 dv[DT], dk[DT];
 #pragma unroll
@@ -249,7 +255,19 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_main_kernel(
       d_n = tid < nq ? Dsum[bh * Nq + q0 + tid] : 0.f;
     }
   };
-  if (n_items > 0) fetch(0);
+  auto stage = [&]() __attribute__((always_inline)) {
+    qn.store(Qs, tid);
+    don.store(dOs, tid);
+    if (tid < 64) {
+      // A row without keys (LSE = -inf) or past Nq gets P = 0: exp2(-inf).
+      lse2[tid] = lse_n > kNegInf ? lse_n * kLog2e : __builtin_huge_valf();
+      dsum[tid] = d_n;
+    }
+  };
+  if (n_items > 0) {
+    fetch(0);
+    stage();
+  }
 
   const int key = k0 + kw;
   for (int item = 0; item < n_items; ++item) {
@@ -258,40 +276,41 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_main_kernel(
     const size_t bh = (size_t)b * Hq + h;
     const int q0 = qb * kBwdBQ;
     const int nq = Nq - q0 < kBwdBQ ? Nq - q0 : kBwdBQ;
-    __syncthreads();  // the previous block's reads of Qs, dOs and dST are done
-    qn.store(Qs, tid);
-    don.store(dOs, tid);
-    if (tid < 64) {
-      // A row without keys (LSE = -inf) or past Nq gets P = 0: exp2(-inf).
-      lse2[tid] = lse_n > kNegInf ? lse_n * kLog2e : __builtin_huge_valf();
-      dsum[tid] = d_n;
-    }
-    if (item + 1 < n_items) fetch(item + 1);
+    // This block's Q, dO, LSE and D are in LDS, and the previous block's
+    // reads of dS^T are done.
     __syncthreads();
+    if (item + 1 < n_items) fetch(item + 1);
 
-    // S and dP for the 64 rows (two 32-row tiles) x this wave's 32 keys.
-    f32x16 s[2], dp[2];
-#pragma unroll
-    for (int qt = 0; qt < 2; ++qt) s[qt] = dp[qt] = f32x16{};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
-        s[qt] = mfma32(row_operand<RS>(Qs, qt * 32, ks * 16, lane), kop[ks], s[qt]);
-        dp[qt] = mfma32(row_operand<RS>(dOs, qt * 32, ks * 16, lane), vop[ks], dp[qt]);
-      }
-
-    // P and dS. C layout: lane l holds key kw, rows qt*32 + 8 (i/4) + 4 hl + i%4.
-    // Elements 8 h2 + 0..7 of a tile are the A operand (k = those rows) of one
-    // 16-row step of dV += P^T dO and dK += dS^T Q; dS^T also goes to LDS for dQ.
-    u32x4 pa[2][2], da[2][2];
     // Masks are needed only at a ragged key block or where the causal
     // diagonal crosses the block (row 0 of the block sees its last key
     // otherwise); rows past Nq have P = 0 through their LSE either way.
     const bool full = nk == kBwdBK && (!causal || k0 + kBwdBK - 1 <= q0 + diag);
-    auto p_ds = [&](auto masked) __attribute__((always_inline)) {
+    // One straight-line body per case, so that the exponentials of one
+    // 32-row tile can be scheduled under the MFMAs of the other.
+    auto tiles = [&](auto masked) __attribute__((always_inline)) {
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt)
+      for (int qt = 0; qt < 2; ++qt) {
+        // S and dP: 32 rows x this wave's 32 keys. All A operands of a
+        // product are read before its MFMAs (one wave per SIMD: nothing
+        // else hides the LDS latency), dO's while the S MFMAs run.
+        bf16x8 opa[KS];
+        f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) opa[ks] = row_operand<RS>(Qs, qt * 32, ks * 16, lane);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) s = mfma32(opa[ks], kop[ks], s);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) opa[ks] = row_operand<RS>(dOs, qt * 32, ks * 16, lane);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) dp = mfma32(opa[ks], vop[ks], dp);
+        __builtin_amdgcn_sched_barrier(0);
+
+        // P and dS. C layout: lane l holds key kw, rows qt*32 + 8 (i/4) + 4 hl + i%4.
+        // Elements 8 h2 + 0..7 are the A operand (k = those rows) of one
+        // 16-row step of dV += P^T dO and dK += dS^T Q; dS^T also goes to LDS for dQ.
+        u32x4 pa[2], da[2];
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
           const int ql = qt * 32 + i4 * 8 + hl * 4;
@@ -301,44 +320,55 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_main_kernel(
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const int i = i4 * 4 + j;
-            float p = fast_exp2(__builtin_fmaf(s[qt][i], sl2, -l4[j]));
+            float x = __builtin_fmaf(s[i], sl2, -l4[j]);
             if (decltype(masked)::value) {
               const bool vis = key < Nk && (!causal || key <= q0 + ql + j + diag);
-              p = vis ? p : 0.f;
+              x = vis ? x : kNegInf;
             }
-            pv[j] = p;
-            dsv[j] = p * (dp[qt][i] - d4[j]);
+            pv[j] = fast_exp2(x);
+            dsv[j] = pv[j] * (dp[i] - d4[j]);
           }
           const uint32_t p0 = pack_bf16x2(pv[0], pv[1]), p1 = pack_bf16x2(pv[2], pv[3]);
           const uint32_t d0 = pack_bf16x2(dsv[0], dsv[1]), d1 = pack_bf16x2(dsv[2], dsv[3]);
-          pa[qt][i4 >> 1][(i4 & 1) * 2] = p0;
-          pa[qt][i4 >> 1][(i4 & 1) * 2 + 1] = p1;
-          da[qt][i4 >> 1][(i4 & 1) * 2] = d0;
-          da[qt][i4 >> 1][(i4 & 1) * 2 + 1] = d1;
+          pa[i4 >> 1][(i4 & 1) * 2] = p0;
+          pa[i4 >> 1][(i4 & 1) * 2 + 1] = p1;
+          da[i4 >> 1][(i4 & 1) * 2] = d0;
+          da[i4 >> 1][(i4 & 1) * 2 + 1] = d1;
           *reinterpret_cast<u32x2*>(dST + kw * kPStride + ql) = u32x2{d0, d1};
         }
-    };
-    if (full)
-      p_ds(std::false_type{});
-    else
-      p_ds(std::true_type{});
-
-    // dV += P^T dO and dK += dS^T Q: this wave's 32 keys x all of d, B operands
-    // read in the row order of the A operands.
+        // dV += P^T dO and dK += dS^T Q: this wave's 32 keys x all of d, B
+        // operands read in the row order of the A operands, all of a 16-row
+        // step before its MFMAs.
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt)
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const bf16x8 ap = __builtin_bit_cast(bf16x8, pa[h2]);
+          const bf16x8 as = __builtin_bit_cast(bf16x8, da[h2]);
+          const int r0 = qt * 32 + h2 * 16;
+          bf16x8 bo[DT], bq[DT];
 #pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        const bf16x8 ap = __builtin_bit_cast(bf16x8, pa[qt][h2]);
-        const bf16x8 as = __builtin_bit_cast(bf16x8, da[qt][h2]);
-        const int r0 = qt * 32 + h2 * 16;
+          for (int dt = 0; dt < DT; ++dt) {
+            bo[dt] = col_operand_c<RS>(dOs, r0, dt * 32, lane);
+            bq[dt] = col_operand_c<RS>(Qs, r0, dt * 32, lane);
+          }
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          dv[dt] = mfma32(ap, col_operand_c<RS>(dOs, r0, dt * 32, lane), dv[dt]);
-          dk[dt] = mfma32(as, col_operand_c<RS>(Qs, r0, dt * 32, lane), dk[dt]);
+          for (int dt = 0; dt < DT; ++dt) {
+            dv[dt] = mfma32(ap, bo[dt], dv[dt]);
+            dk[dt] = mfma32(as, bq[dt], dk[dt]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
-    __syncthreads();  // dS^T of all 128 keys is in LDS
+    };
+    if (full)
+      tiles(std::false_type{});
+    else
+      tiles(std::true_type{});
+    // dS^T of all 128 keys is in LDS, and Qs, dOs, LSE and D are no longer
+    // read: the next block goes in now, before this block's dQ atomics, so
+    // that waiting for its loads never waits for those adds as well.
+    __syncthreads();
+    if (item + 1 < n_items) stage();
 
     // dQ rows half*32.. (+ q0), d blocks dh*(D/2) + 32 i: dS K over the 128 keys.
     f32x16 dq[L::DB];
