@@ -142,9 +142,10 @@ def bench_prefill_fp8(w, steps, warmup, device, min_warm_s=0.2):
 
 
 def bench_backward(w, steps, warmup, device, min_warm_s=0.2):
-    """fa_bwd (prep, main, dQ convert) with O and LSE from one fa_fwd outside
-    the timed steps; dO seeded like the inputs. FLOPs: the five products,
-    2.5 times the forward's."""
+    """fa_bwd (D, then the dK/dV and dQ kernels) with O and LSE from one fa_fwd
+    outside the timed steps; dO seeded like the inputs. FLOPs: the five
+    products of the chain rule, 2.5 times the forward's (the dQ kernel computes
+    S and dP a second time: 3.5 times the forward's MFMA work is executed)."""
     import torch
     import exact_io_aware_17_amd as fa
     q, k, v = device_inputs(w, device)
@@ -406,7 +407,7 @@ def main():
                                   "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                                   "frac": round(rb["kernel_tflops"] / PEAK_BF16_TFLOPS, 4), "traffic": bwd_traffic,
                                   "kernel_ms": round(rb["kernel_ms"], 5),
-                                  "kernel": "bwd_prep_kernel<128> + bwd_main_kernel<128> + bwd_dq_kernel"}},
+                                  "kernel": "bwd_prep_kernel<128> + bwd_dkdv_kernel<128> + bwd_dq_kernel<128>"}},
         "decode": {"workload": wd.name, "metric": "decode HBM GB/s (algorithmic bytes / step time)",
                    "value": round(rd["gbs"], 1), "unit": "GB/s", "ms_per_step": round(rd["ms_per_step"], 5),
                    "roofline": {"bound": "hbm", "achieved": round(rd["kernel_gbs"], 1), "peak": PEAK_HBM_GBS,

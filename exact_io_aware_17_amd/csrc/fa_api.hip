@@ -62,12 +62,11 @@ bool split_ws_sizes(int B, int Hq, int Nq, int d, int S, size_t* o_bytes, size_t
 
 // Workspace of the backward pass: fp32 dQ accumulator, then (256-aligned)
 // the fp32 row sums D.
-bool bwd_ws_sizes(int B, int Hq, int Nq, int d, size_t* acc_bytes, size_t* total) {
+bool bwd_ws_sizes(int B, int Hq, int Nq, int d, size_t* total) {
   if (B < 0 || Hq < 1 || Nq < 0 || (d != 64 && d != 128)) return false;
   const long long rows = elems4(B, Hq, Nq, 1);
   if (rows < 0 || rows > (1LL << 50)) return false;
-  *acc_bytes = round256((size_t)rows * (size_t)d * 4u);
-  *total = *acc_bytes + round256((size_t)rows * 4u);
+  *total = round256((size_t)rows * 4u);  // fp32 D per row
   return true;
 }
 
@@ -126,8 +125,8 @@ fa_status fa_fwd_fp8(const void* q, const void* k, const void* v, float q_descal
 }
 
 size_t fa_bwd_workspace_bytes(int B, int Hq, int Nq, int d) {
-  size_t ab = 0, total = 0;
-  if (!bwd_ws_sizes(B, Hq, Nq, d, &ab, &total)) return 0;
+  size_t total = 0;
+  if (!bwd_ws_sizes(B, Hq, Nq, d, &total)) return 0;
   return total;
 }
 
@@ -142,18 +141,17 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
   if (nkv > 0 && (!dk || !dv)) return FA_ERR_NULL;
   for (const void* p : {dout, (const void*)dq, (const void*)dk, (const void*)dv})
     if (p && !aligned16(p)) return FA_ERR_ALIGN;
-  size_t ab = 0, total = 0;
-  if (!bwd_ws_sizes(B, Hq, Nq, d, &ab, &total)) return FA_ERR_SHAPE;
+  size_t total = 0;
+  if (!bwd_ws_sizes(B, Hq, Nq, d, &total)) return FA_ERR_SHAPE;
   if (nq > 0) {
     if (!workspace || workspace_bytes < total) return FA_ERR_WORKSPACE;
     if (((uintptr_t)workspace & 255u) != 0) return FA_ERR_ALIGN;
   }
-  if (fa::bwd_grid(B, Hkv, Nk) > kMaxGridX || (long long)B * Hq * Nq / 4 + 1 > kMaxGridX ||
-      nq / 1024 + 1 > kMaxGridX)
+  if (fa::bwd_grid(B, Hkv, Nk) > kMaxGridX || (long long)B * Hq * Nq / 4 + 1 > kMaxGridX)
     return FA_ERR_UNSUPPORTED;
   if (nq == 0 && nkv == 0) return FA_OK;
   fa::FwdArgs f{q, k, v, nullptr, const_cast<float*>(lse), B, Hq, Hkv, Nq, Nk, d, scale, causal, stream};
-  fa::BwdArgs a{f, o, dout, dq, dk, dv, (float*)workspace, (float*)((char*)workspace + ab)};
+  fa::BwdArgs a{f, o, dout, dq, dk, dv, (float*)workspace};
   return launched(fa::launch_bwd(a));
 }
 

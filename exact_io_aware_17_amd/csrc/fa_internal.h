@@ -48,8 +48,7 @@ struct BwdArgs {
   void* dq;          // [B, Hq, Nq, d] bf16
   void* dk;          // [B, Hkv, Nk, d] bf16
   void* dv;          // [B, Hkv, Nk, d] bf16
-  float* dq_acc;     // workspace: fp32 [B, Hq, Nq, d]
-  float* dsum;       // workspace: fp32 [B, Hq, Nq]
+  float* dsum;       // workspace: fp32 D [B, Hq, Nq]
 };
 
 hipError_t launch_fwd_bf16(const FwdArgs& a);       // d = 64, 128

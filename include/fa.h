@@ -108,9 +108,9 @@ fa_status fa_fwd_fp8(const void* q, const void* k, const void* v,
                      float scale, int causal, void* stream);
 
 /*
- * fa_bwd_workspace_bytes -- bytes of workspace fa_bwd needs: an fp32 dQ
- * accumulator [B,Hq,Nq,d] followed (at the next 256-byte boundary) by the
- * fp32 row sums D [B,Hq,Nq].  Returns 0 for invalid sizes.
+ * fa_bwd_workspace_bytes -- bytes of workspace fa_bwd needs: the fp32 row
+ * sums D [B,Hq,Nq], rounded up to a multiple of 256.  Returns 0 for invalid
+ * sizes (and for Nq = 0).
  */
 size_t fa_bwd_workspace_bytes(int B, int Hq, int Nq, int d);
 
@@ -128,8 +128,10 @@ size_t fa_bwd_workspace_bytes(int B, int Hq, int Nq, int d);
  * q, o, dout, dq [B,Hq,Nq,d] bf16; k, v, dk, dv [B,Hkv,Nk,d] bf16; lse
  * [B,Hq,Nq] fp32 as written by fa_fwd with the same q, k, v, scale, causal.
  * Products run on bf16 matrix cores with fp32 accumulation; P and dS are
- * rounded to bf16 as MFMA operands, D and the softmax are fp32, dQ is
- * accumulated in fp32 in the workspace before its bf16 rounding.
+ * rounded to bf16 as MFMA operands, D and the softmax are fp32.  dQ is
+ * accumulated in registers over all keys (S and dP are computed a second
+ * time for it) and rounded to bf16 once; no atomics are used, so the result
+ * does not depend on scheduling.
  * d must be 64 or 128.  workspace (device, caller-owned, 256-byte aligned)
  * of at least fa_bwd_workspace_bytes(B,Hq,Nq,d) bytes; its contents are
  * overwritten.  Other rules as fa_fwd; outputs must not overlap the inputs.

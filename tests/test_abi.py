@@ -101,7 +101,8 @@ def test_fp8_argument_checks():
 def test_bwd_workspace_and_argument_checks():
     """Host-side checks of fa_bwd; every rejected call returns before a launch."""
     lib = fa.lib()
-    assert lib.fa_bwd_workspace_bytes(2, 3, 5, 128) == 15360 + 256  # 30 rows * 128 * 4, then 30 * 4 rounded up to 256
+    assert lib.fa_bwd_workspace_bytes(2, 3, 5, 128) == 256  # D of 30 rows, 120 bytes rounded up to 256
+    assert lib.fa_bwd_workspace_bytes(1, 2, 100, 64) == 1024  # 800 bytes rounded up
     assert lib.fa_bwd_workspace_bytes(1, 1, 0, 64) == 0 + 0
     assert lib.fa_bwd_workspace_bytes(1, 1, 4, 96) == 0
     assert lib.fa_bwd_workspace_bytes(-1, 1, 4, 64) == 0
