@@ -60,8 +60,7 @@ bool split_ws_sizes(int B, int Hq, int Nq, int d, int S, size_t* o_bytes, size_t
   return true;
 }
 
-// Workspace of the backward pass: fp32 dQ accumulator, then (256-aligned)
-// the fp32 row sums D.
+// Workspace of the backward pass: the fp32 row sums D.
 bool bwd_ws_sizes(int B, int Hq, int Nq, int d, size_t* total) {
   if (B < 0 || Hq < 1 || Nq < 0 || (d != 64 && d != 128)) return false;
   const long long rows = elems4(B, Hq, Nq, 1);
