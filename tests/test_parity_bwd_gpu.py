@@ -118,3 +118,20 @@ def test_bwd_degenerate_sizes():
         torch.cuda.synchronize()
         for t in (dq, dk, dv):
             assert t.numel() == 0 or float(t.float().abs().max()) == 0.0
+
+
+def test_bwd_deterministic():
+    """Every gradient element is written once by one lane (no atomics), so two
+    calls on the same inputs agree bit for bit."""
+    import torch
+    import exact_io_aware_17_amd as fa
+    w = synth.Workload("bwd_determinism", 2, 4, 2, 300, 517, 128, causal=True)
+    say("case bwd determinism")
+    q, k, v = (_dev_bf16(w.seed, t, s) for t, s in ((0, w.q_shape), (1, w.kv_shape), (2, w.kv_shape)))
+    do = _dev_bf16(w.seed, synth.TENSOR_DO, w.q_shape)
+    o, lse = fa.forward(q, k, v, causal=True, scale=w.scale)
+    first = fa.backward(q, k, v, o, lse, do, causal=True, scale=w.scale)
+    second = fa.backward(q, k, v, o, lse, do, causal=True, scale=w.scale)
+    torch.cuda.synchronize()
+    for a, b in zip(first, second):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
