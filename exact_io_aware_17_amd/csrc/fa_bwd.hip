@@ -39,10 +39,10 @@
 //    that bounded the whole pass.
 //  Column-wise operands (dO, Q and K read across rows) come from the
 //  transposing LDS read ds_read_b64_tr_b16 (lane semantics in fa_common.h);
-//  rows are padded by 16 bytes so that row-wise 16-byte reads of 16
-//  consecutive rows touch distinct banks. All A operands of a product are
-//  read before its MFMAs (with one wave per SIMD nothing else hides the LDS
-//  latency).
+//  rows are padded so that row-wise 16-byte reads of 16 consecutive rows
+//  touch distinct banks and the transposing reads are at most 2-way. All
+//  LDS operands of a product are read before its MFMAs (with one wave per
+//  SIMD nothing else hides the LDS latency).
 #include <type_traits>
 
 #include "fa_common.h"
@@ -59,7 +59,11 @@ constexpr int kDqBK = 64;     // dQ kernel: keys per block
 
 template <int D>
 struct BwdLayout {
-  static constexpr int RS = D + 8;  // row stride of the Q, dO, K and V tiles (elements)
+  // Row stride of the Q, dO, K and V tiles (elements). The padding sets the
+  // bank shift between rows (64 banks of 4 bytes): 48 bytes at d = 128 leave
+  // the 16-byte row reads conflict-free and the transposing reads 2-way
+  // (16 bytes: 4-way), 16 bytes at d = 64 give the same.
+  static constexpr int RS = D == 128 ? D + 24 : D + 8;
   static constexpr int TILE = kBwdBQ * RS;  // one 64-row tile
   static constexpr int KS = D / 16;  // 16-wide d steps of S and dP
   static constexpr int DT = D / 32;  // 32-wide d tiles of dK, dV and dQ (each wave: all of d)
