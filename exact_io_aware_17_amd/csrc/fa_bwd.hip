@@ -437,59 +437,86 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(
     // Masks only at a ragged key block or where the causal diagonal crosses
     // the block for the workgroup's first row.
     const bool full = k0 + kDqBK <= Nk && (!causal || k0 + kDqBK - 1 <= q0 + diag);
-    auto tiles = [&](auto masked) __attribute__((always_inline)) {
+    // S^T and dP^T of a 32-key tile: 32 keys x this wave's 32 rows.
+    // The V rows are read while the S^T MFMAs run.
+    auto sdp = [&](int kt, f32x16& st, f32x16& dpt) __attribute__((always_inline)) {
+      bf16x8 opa[KS];
 #pragma unroll
-      for (int kt = 0; kt < kDqBK / 32; ++kt) {
-        // S^T and dP^T: 32 keys x this wave's 32 rows.
-        bf16x8 opa[KS];
-        f32x16 st = f32x16{}, dpt = f32x16{};
+      for (int ks = 0; ks < KS; ++ks) opa[ks] = row_operand<RS>(Ks, kt * 32, ks * 16, lane);
+      __builtin_amdgcn_sched_barrier(0);
+      st = dpt = f32x16{};
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) opa[ks] = row_operand<RS>(Ks, kt * 32, ks * 16, lane);
-        __builtin_amdgcn_sched_barrier(0);
+      for (int ks = 0; ks < KS; ++ks) st = mfma32(opa[ks], qop[ks], st);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) st = mfma32(opa[ks], qop[ks], st);
+      for (int ks = 0; ks < KS; ++ks) opa[ks] = row_operand<RS>(Vs, kt * 32, ks * 16, lane);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) opa[ks] = row_operand<RS>(Vs, kt * 32, ks * 16, lane);
-        __builtin_amdgcn_sched_barrier(0);
+      for (int ks = 0; ks < KS; ++ks) dpt = mfma32(opa[ks], dop[ks], dpt);
+    };
+    // dS^T. C layout: lane l holds row qw, keys k0 + kt*32 + 8 (i/4) + 4 hl + i%4;
+    // elements 8 h2 + 0..7 are the B operand (k = those keys) of one 16-key
+    // step of dQ^T += K^T dS^T.
+    auto ds_t = [&](auto masked, int kt, const f32x16& st, const f32x16& dpt, u32x4* bs) __attribute__((always_inline)) {
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) dpt = mfma32(opa[ks], dop[ks], dpt);
-        __builtin_amdgcn_sched_barrier(0);
-
-        // dS^T. C layout: lane l holds row qw, keys k0 + kt*32 + 8 (i/4) + 4 hl + i%4;
-        // elements 8 h2 + 0..7 are the B operand (k = those keys) of one
-        // 16-key step of dQ^T += K^T dS^T.
-        u32x4 bs[2];
+      for (int i4 = 0; i4 < 4; ++i4) {
+        float dsv[4];
 #pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          float dsv[4];
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const int i = i4 * 4 + jj;
-            float x = __builtin_fmaf(st[i], sl2, -l2);
-            if (decltype(masked)::value) {
-              const int key = k0 + kt * 32 + i4 * 8 + hl * 4 + jj;
-              const bool vis = key < Nk && (!causal || key <= qw + diag);
-              x = vis ? x : kNegInf;
-            }
-            dsv[jj] = fast_exp2(x) * (dpt[i] - drow);
+        for (int jj = 0; jj < 4; ++jj) {
+          const int i = i4 * 4 + jj;
+          float x = __builtin_fmaf(st[i], sl2, -l2);
+          if (decltype(masked)::value) {
+            const int key = k0 + kt * 32 + i4 * 8 + hl * 4 + jj;
+            const bool vis = key < Nk && (!causal || key <= qw + diag);
+            x = vis ? x : kNegInf;
           }
-          bs[i4 >> 1][(i4 & 1) * 2] = pack_bf16x2(dsv[0], dsv[1]);
-          bs[i4 >> 1][(i4 & 1) * 2 + 1] = pack_bf16x2(dsv[2], dsv[3]);
+          dsv[jj] = fast_exp2(x) * (dpt[i] - drow);
         }
-        // dQ^T += K^T dS^T: A operand K read across key rows in the order of
-        // the B operand's elements.
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          const bf16x8 bsv = __builtin_bit_cast(bf16x8, bs[h2]);
-          bf16x8 ka[DT];
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt) ka[dt] = col_operand_c<RS>(Ks, kt * 32 + h2 * 16, dt * 32, lane);
-          __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt) dq[dt] = mfma32(ka[dt], bsv, dq[dt]);
-          __builtin_amdgcn_sched_barrier(0);
-        }
+        bs[i4 >> 1][(i4 & 1) * 2] = pack_bf16x2(dsv[0], dsv[1]);
+        bs[i4 >> 1][(i4 & 1) * 2 + 1] = pack_bf16x2(dsv[2], dsv[3]);
       }
+    };
+    // dQ^T += K^T dS^T for one 32-key tile: A operand K read across key rows
+    // in the order of the B operand's elements.
+    auto dq_mm = [&](int kt, const u32x4* bs) __attribute__((always_inline)) {
+      bf16x8 ka[2][DT];
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) ka[h2][dt] = col_operand_c<RS>(Ks, kt * 32 + h2 * 16, dt * 32, lane);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const bf16x8 bsv = __builtin_bit_cast(bf16x8, bs[h2]);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) dq[dt] = mfma32(ka[h2][dt], bsv, dq[dt]);
+      }
+    };
+    // The exponentials of one tile are scheduled between the MFMAs of the
+    // other (a wave issues VALU work while its MFMAs run): tile 0's under
+    // tile 1's S^T and dP^T, tile 1's under tile 0's dQ^T product.
+    auto tiles = [&](auto masked) __attribute__((always_inline)) {
+      f32x16 st0, dpt0, st1, dpt1;
+      u32x4 bs0[2], bs1[2];
+      sdp(0, st0, dpt0);
+      __builtin_amdgcn_sched_barrier(0);
+      sdp(1, st1, dpt1);
+      ds_t(masked, 0, st0, dpt0, bs0);
+#pragma unroll
+      for (int i = 0; i < KS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);  // ten VALU
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      dq_mm(0, bs0);
+      ds_t(masked, 1, st1, dpt1, bs1);
+#pragma unroll
+      for (int i = 0; i < 2 * DT; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(0x002, 10, 1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      dq_mm(1, bs1);
+      __builtin_amdgcn_sched_barrier(0);
     };
     if (full)
       tiles(std::false_type{});
