@@ -259,73 +259,99 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(
     // diagonal crosses the block (row 0 of the block sees its last key
     // otherwise); rows past Nq have P = 0 through their LSE either way.
     const bool full = nk == kBwdBK && (!causal || k0 + kBwdBK - 1 <= q0 + diag);
-    // One straight-line body per case.
-    auto tiles = [&](auto masked) __attribute__((always_inline)) {
+    // S and dP of a 32-row tile: 32 rows x this wave's 32 keys; the dO rows
+    // are read while the S MFMAs run.
+    auto sdp = [&](int qt, f32x16& s, f32x16& dp) __attribute__((always_inline)) {
+      bf16x8 opa[KS];
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
-        // S and dP: 32 rows x this wave's 32 keys.
-        bf16x8 opa[KS];
-        f32x16 s = f32x16{}, dp = f32x16{};
+      for (int ks = 0; ks < KS; ++ks) opa[ks] = row_operand<RS>(Qs, qt * 32, ks * 16, lane);
+      __builtin_amdgcn_sched_barrier(0);
+      s = dp = f32x16{};
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) opa[ks] = row_operand<RS>(Qs, qt * 32, ks * 16, lane);
-        __builtin_amdgcn_sched_barrier(0);
+      for (int ks = 0; ks < KS; ++ks) s = mfma32(opa[ks], kop[ks], s);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) s = mfma32(opa[ks], kop[ks], s);
+      for (int ks = 0; ks < KS; ++ks) opa[ks] = row_operand<RS>(dOs, qt * 32, ks * 16, lane);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) opa[ks] = row_operand<RS>(dOs, qt * 32, ks * 16, lane);
-        __builtin_amdgcn_sched_barrier(0);
+      for (int ks = 0; ks < KS; ++ks) dp = mfma32(opa[ks], vop[ks], dp);
+    };
+    // P and dS. C layout: lane l holds key kw, rows qt*32 + 8 (i/4) + 4 hl + i%4.
+    // Elements 8 h2 + 0..7 are the A operand (k = those rows) of one 16-row
+    // step of dV += P^T dO and dK += dS^T Q.
+    auto p_ds = [&](auto masked, int qt, const f32x16& s, const f32x16& dp, u32x4* pa, u32x4* da)
+                    __attribute__((always_inline)) {
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) dp = mfma32(opa[ks], vop[ks], dp);
-        __builtin_amdgcn_sched_barrier(0);
-
-        // P and dS. C layout: lane l holds key kw, rows qt*32 + 8 (i/4) + 4 hl + i%4.
-        // Elements 8 h2 + 0..7 are the A operand (k = those rows) of one
-        // 16-row step of dV += P^T dO and dK += dS^T Q.
-        u32x4 pa[2], da[2];
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int ql = qt * 32 + i4 * 8 + hl * 4;
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2 + ql);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(dsum + ql);
+        float pv[4], dsv[4];
 #pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const int ql = qt * 32 + i4 * 8 + hl * 4;
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2 + ql);
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(dsum + ql);
-          float pv[4], dsv[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int i = i4 * 4 + j;
-            float x = __builtin_fmaf(s[i], sl2, -l4[j]);
-            if (decltype(masked)::value) {
-              const bool vis = key < Nk && (!causal || key <= q0 + ql + j + diag);
-              x = vis ? x : kNegInf;
-            }
-            pv[j] = fast_exp2(x);
-            dsv[j] = pv[j] * (dp[i] - d4[j]);
+        for (int j = 0; j < 4; ++j) {
+          const int i = i4 * 4 + j;
+          float x = __builtin_fmaf(s[i], sl2, -l4[j]);
+          if (decltype(masked)::value) {
+            const bool vis = key < Nk && (!causal || key <= q0 + ql + j + diag);
+            x = vis ? x : kNegInf;
           }
-          pa[i4 >> 1][(i4 & 1) * 2] = pack_bf16x2(pv[0], pv[1]);
-          pa[i4 >> 1][(i4 & 1) * 2 + 1] = pack_bf16x2(pv[2], pv[3]);
-          da[i4 >> 1][(i4 & 1) * 2] = pack_bf16x2(dsv[0], dsv[1]);
-          da[i4 >> 1][(i4 & 1) * 2 + 1] = pack_bf16x2(dsv[2], dsv[3]);
+          pv[j] = fast_exp2(x);
+          dsv[j] = pv[j] * (dp[i] - d4[j]);
         }
-        // dV += P^T dO and dK += dS^T Q: this wave's 32 keys x all of d, B
-        // operands read in the row order of the A operands.
+        pa[i4 >> 1][(i4 & 1) * 2] = pack_bf16x2(pv[0], pv[1]);
+        pa[i4 >> 1][(i4 & 1) * 2 + 1] = pack_bf16x2(pv[2], pv[3]);
+        da[i4 >> 1][(i4 & 1) * 2] = pack_bf16x2(dsv[0], dsv[1]);
+        da[i4 >> 1][(i4 & 1) * 2 + 1] = pack_bf16x2(dsv[2], dsv[3]);
+      }
+    };
+    // dV += P^T dO and dK += dS^T Q: this wave's 32 keys x all of d, B
+    // operands read in the row order of the A operands.
+    auto dvdk = [&](int qt, const u32x4* pa, const u32x4* da) __attribute__((always_inline)) {
 #pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          const bf16x8 ap = __builtin_bit_cast(bf16x8, pa[h2]);
-          const bf16x8 as = __builtin_bit_cast(bf16x8, da[h2]);
-          const int r0 = qt * 32 + h2 * 16;
-          bf16x8 bo[DT], bq[DT];
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const bf16x8 ap = __builtin_bit_cast(bf16x8, pa[h2]);
+        const bf16x8 as = __builtin_bit_cast(bf16x8, da[h2]);
+        const int r0 = qt * 32 + h2 * 16;
+        bf16x8 bo[DT], bq[DT];
 #pragma unroll
-          for (int dt = 0; dt < DT; ++dt) {
-            bo[dt] = col_operand_c<RS>(dOs, r0, dt * 32, lane);
-            bq[dt] = col_operand_c<RS>(Qs, r0, dt * 32, lane);
-          }
-          __builtin_amdgcn_sched_barrier(0);
+        for (int dt = 0; dt < DT; ++dt) {
+          bo[dt] = col_operand_c<RS>(dOs, r0, dt * 32, lane);
+          bq[dt] = col_operand_c<RS>(Qs, r0, dt * 32, lane);
+        }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int dt = 0; dt < DT; ++dt) {
-            dv[dt] = mfma32(ap, bo[dt], dv[dt]);
-            dk[dt] = mfma32(as, bq[dt], dk[dt]);
-          }
-          __builtin_amdgcn_sched_barrier(0);
+        for (int dt = 0; dt < DT; ++dt) {
+          dv[dt] = mfma32(ap, bo[dt], dv[dt]);
+          dk[dt] = mfma32(as, bq[dt], dk[dt]);
         }
       }
+    };
+    // One straight-line body per case. The exponentials of one tile are
+    // scheduled between the MFMAs of the other (a wave issues VALU work while
+    // its MFMAs run): tile 0's under tile 1's dP, tile 1's under tile 0's
+    // second dV/dK step.
+    auto tiles = [&](auto masked) __attribute__((always_inline)) {
+      f32x16 s0, dp0, s1, dp1;
+      u32x4 pa0[2], da0[2], pa1[2], da1[2];
+      sdp(0, s0, dp0);
+      __builtin_amdgcn_sched_barrier(0);
+      sdp(1, s1, dp1);
+      p_ds(masked, 0, s0, dp0, pa0, da0);
+#pragma unroll
+      for (int i = 0; i < KS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);  // ten VALU
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      dvdk(0, pa0, da0);
+      p_ds(masked, 1, s1, dp1, pa1, da1);
+#pragma unroll
+      for (int i = 0; i < 2 * DT; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(0x002, 10, 1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      dvdk(1, pa1, da1);
+      __builtin_amdgcn_sched_barrier(0);
     };
     if (full)
       tiles(std::false_type{});
