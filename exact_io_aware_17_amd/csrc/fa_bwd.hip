@@ -10,21 +10,26 @@
 //
 // Kernels (no atomics: every output element is written by one lane):
 //  * bwd_prep_kernel: D_i in fp32 (workspace).
-//  * bwd_dkdv_kernel: one workgroup (4 waves) per (batch, KV head, 128-key
-//    block); each wave owns 32 keys. Their K and V rows stay in registers as
-//    the B operands of S = Q K^T and dP = dO V^T. The workgroup walks the
-//    query heads of its GQA group and their 64-row query blocks (under the
-//    causal mask only the blocks that see a key of the block), Q, dO, LSE
-//    and D double-buffered in LDS (the next block's rows are loaded into
-//    registers while the current one is computed). Per 32-row tile:
-//      - S and dP (32 rows x the wave's 32 keys) with 32x32x16 bf16 MFMAs;
+//  * bwd_dkdv_kernel: one workgroup (8 waves, two per SIMD) per (batch, KV
+//    head, 128-key block). Waves w and w + 4 share 32 keys, whose K rows stay
+//    in registers as the B operands of S = Q K^T (V sits in LDS for
+//    dP = dO V^T). The workgroup walks the query heads of its GQA group and
+//    their 64-row query blocks (under the causal mask only the blocks that
+//    see a key of the block), Q, dO, LSE and D double-buffered in LDS (the
+//    next block's rows are loaded into registers while the current one is
+//    computed). Per query block:
+//      - wave w + 4 r computes, for the 32-row half r of the block, S and dP
+//        (32 rows x the pair's 32 keys) with 32x32x16 bf16 MFMAs;
 //        P = exp2(S scale log2e - LSE log2e), dS = P (dP - D) in fp32,
 //        masked entries 0 (masks only where a ragged or diagonal block
 //        needs them);
-//      - P and dS stay in registers: in the MFMA result each lane holds one
-//        key and 16 rows, which is the A operand of dV += P^T dO and
-//        dK += dS^T Q once dO and Q are read in that row order; dK and dV
-//        (32 keys x d per wave) accumulate in registers.
+//      - in the MFMA result each lane holds one key and 16 rows, which is
+//        the A operand of dV += P^T dO and dK += dS^T Q once dO and Q are
+//        read in that row order: the pair swaps these bf16 operands through
+//        LDS, and each wave accumulates dK and dV over all 64 rows for its
+//        half of d (32 keys x d/2 in registers), so that a wave fits in half
+//        of the SIMD's registers and one wave's softmax runs under the
+//        other's MFMAs.
 //  * bwd_dq_kernel: one workgroup (4 waves) per (batch, query head, 128-row
 //    block); each wave owns 32 rows, whose Q and dO stay in registers. S and
 //    dP are recomputed transposed, S^T = K Q^T and dP^T = V dO^T, 64 keys at
@@ -51,7 +56,8 @@
 namespace fa {
 namespace {
 
-constexpr int kBwdThreads = 256;
+constexpr int kBwdThreads = 256;   // dQ kernel: 4 waves
+constexpr int kDkdvThreads = 512;  // dK/dV kernel: 8 waves, two per SIMD
 constexpr int kBwdBQ = 64;    // dK/dV kernel: query rows per block
 constexpr int kBwdBK = 128;   // dK/dV kernel: keys per workgroup (32 per wave)
 constexpr int kDqRows = 128;  // dQ kernel: query rows per workgroup (32 per wave)
@@ -98,23 +104,23 @@ __device__ __forceinline__ bf16x8 row_operand(const uint16_t* tile, int r0, int 
 // rows zero) in two halves: global loads into registers (issued one block
 // ahead, so that their latency hides under the current block's work), then
 // the stores into the tile.
-template <int D>
+template <int D, int NT = kBwdThreads>
 struct RowsInFlight {
   static constexpr int CH = D / 8;
-  static constexpr int N = 64 * CH / kBwdThreads;
+  static constexpr int N = 64 * CH / NT;
   u32x4 r[N];
   __device__ __forceinline__ void load(const uint16_t* __restrict__ src, int nrows, int tid) {
     if (nrows == 64) {
 #pragma unroll
       for (int i = 0; i < N; ++i) {
-        const int id = tid + i * kBwdThreads;
+        const int id = tid + i * NT;
         r[i] = *reinterpret_cast<const u32x4*>(src + (size_t)(id / CH) * D + (id % CH) * 8);
       }
       return;
     }
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-      const int id = tid + i * kBwdThreads;
+      const int id = tid + i * NT;
       const int row = id / CH, ch = id % CH;
       r[i] = row < nrows ? *reinterpret_cast<const u32x4*>(src + (size_t)row * D + ch * 8) : u32x4{0u, 0u, 0u, 0u};
     }
@@ -122,7 +128,7 @@ struct RowsInFlight {
   __device__ __forceinline__ void store(uint16_t* tile, int tid) const {
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-      const int id = tid + i * kBwdThreads;
+      const int id = tid + i * NT;
       *reinterpret_cast<u32x4*>(tile + (id / CH) * BwdLayout<D>::RS + (id % CH) * 8) = r[i];
     }
   }
@@ -154,16 +160,21 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restric
 __device__ __forceinline__ void wait_vm_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 template <int D>
-__global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(kDkdvThreads) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dsum,
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int Hq, int Hkv, int Nq, int Nk, float scale, float sl2,
     int causal, int n_kb) {
   using L = BwdLayout<D>;
-  constexpr int RS = L::RS, KS = L::KS, DT = L::DT;
-  // [buffer][Q, dO] tiles, then [buffer][LSE * log2e, D] rows of 64 floats.
-  __shared__ __attribute__((aligned(16))) uint16_t lds[4 * L::TILE + 2 * 2 * 64 * 2];
-  float* rowv = reinterpret_cast<float*>(lds + 4 * L::TILE);
+  constexpr int RS = L::RS, KS = L::KS, DH = L::DT / 2;
+  // [buffer][Q, dO] tiles; the block's 128 V rows; per wave 64 lanes x 64
+  // bytes of P and dS operands for its partner; [buffer][LSE * log2e, D]
+  // rows of 64 floats.
+  constexpr int XCH = 8 * 64 * 32;  // bf16 elements of the operand exchange
+  __shared__ __attribute__((aligned(16))) uint16_t lds[6 * L::TILE + XCH + 2 * 2 * 64 * 2];
+  uint16_t* Vs = lds + 4 * L::TILE;
+  u32x4* xch = reinterpret_cast<u32x4*>(lds + 6 * L::TILE);
+  float* rowv = reinterpret_cast<float*>(lds + 6 * L::TILE + XCH);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -184,23 +195,36 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(
   const uint16_t* Vh = V + ((size_t)(b * Hkv + g) * Nk + k0) * D;
   const int diag = Nk - Nq;
 
-  // This wave's 32 keys as the B operands of S = Q K^T and dP = dO V^T:
-  // lane l holds key wave*32 + l%32, d = 16 ks + 8 (l/32) + 0..7.
-  const int kw = wave * 32 + (lane & 31);
-  bf16x8 kop[KS], vop[KS];
+  // Waves w and w + 4 (one SIMD) share 32 keys: wave w computes S, dP, P
+  // and dS for rows 0..31 of each query block and wave w + 4 for rows
+  // 32..63; they swap the bf16 P and dS operands through LDS, and each then
+  // accumulates dK and dV over all 64 rows for one half of d. So a wave needs
+  // half the accumulators and fits in half of the SIMD's registers, and the
+  // two waves of a SIMD overlap one's softmax with the other's MFMAs.
+  // K rows are the B operands of S = Q K^T (lane l holds key kg*32 + l%32,
+  // d = 16 ks + 8 (l/32) + 0..7); V goes to LDS for dP = dO V^T (keys past Nk
+  // are zero).
+  const int kg = wave & 3, role = wave >> 2;
+  const int kw = kg * 32 + (lane & 31);
+  bf16x8 kop[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
-    kop[ks] = vop[ks] = bf16x8{};
-    if (kw < nk) {
-      kop[ks] = *reinterpret_cast<const bf16x8*>(Kh + (size_t)kw * D + ks * 16 + hl * 8);
-      vop[ks] = *reinterpret_cast<const bf16x8*>(Vh + (size_t)kw * D + ks * 16 + hl * 8);
+    kop[ks] = bf16x8{};
+    if (kw < nk) kop[ks] = *reinterpret_cast<const bf16x8*>(Kh + (size_t)kw * D + ks * 16 + hl * 8);
+  }
+  {
+    RowsInFlight<D, kDkdvThreads> vr;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      vr.load(Vh + (size_t)h * 64 * D, nk - h * 64, tid);
+      vr.store(Vs + h * 64 * RS, tid);
     }
   }
   wait_vm_loads();
 
-  f32x16 dv[DT], dk[DT];
+  f32x16 dv[DH], dk[DH];
 #pragma unroll
-  for (int i = 0; i < DT; ++i) dv[i] = dk[i] = f32x16{};
+  for (int i = 0; i < DH; ++i) dv[i] = dk[i] = f32x16{};
 
   // Query blocks that see a key of this block: under the causal mask, row i
   // sees key j iff j <= i + diag, so rows below k0 - diag see none.
@@ -213,7 +237,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(
   // Work items: (query head of the group, query block), query block fastest.
   const int per_head = n_qb > qb0 ? n_qb - qb0 : 0;
   const int n_items = group * per_head;
-  RowsInFlight<D> qn, don;
+  RowsInFlight<D, kDkdvThreads> qn, don;
   float lse_n = kNegInf, d_n = 0.f;
   auto fetch = [&](int item) __attribute__((always_inline)) {
     const int hh = item / per_head, qb = qb0 + item % per_head;
@@ -262,18 +286,28 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(
     // S and dP of a 32-row tile: 32 rows x this wave's 32 keys; the dO rows
     // are read while the S MFMAs run.
     auto sdp = [&](int qt, f32x16& s, f32x16& dp) __attribute__((always_inline)) {
-      bf16x8 opa[KS];
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) opa[ks] = row_operand<RS>(Qs, qt * 32, ks * 16, lane);
-      __builtin_amdgcn_sched_barrier(0);
       s = dp = f32x16{};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) s = mfma32(opa[ks], kop[ks], s);
+      for (int h = 0; h < 2; ++h) {
+        bf16x8 opa[KS / 2];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) opa[ks] = row_operand<RS>(dOs, qt * 32, ks * 16, lane);
-      __builtin_amdgcn_sched_barrier(0);
+        for (int k = 0; k < KS / 2; ++k) opa[k] = row_operand<RS>(Qs, qt * 32, (h * KS / 2 + k) * 16, lane);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) dp = mfma32(opa[ks], vop[ks], dp);
+        for (int k = 0; k < KS / 2; ++k) s = mfma32(opa[k], kop[h * KS / 2 + k], s);
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        bf16x8 opa[KS / 2], opb[KS / 2];
+#pragma unroll
+        for (int k = 0; k < KS / 2; ++k) {
+          opa[k] = row_operand<RS>(dOs, qt * 32, (h * KS / 2 + k) * 16, lane);
+          opb[k] = row_operand<RS>(Vs, kg * 32, (h * KS / 2 + k) * 16, lane);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int k = 0; k < KS / 2; ++k) dp = mfma32(opa[k], opb[k], dp);
+      }
     };
     // P and dS. C layout: lane l holds key kw, rows qt*32 + 8 (i/4) + 4 hl + i%4.
     // Elements 8 h2 + 0..7 are the A operand (k = those rows) of one 16-row
@@ -311,62 +345,61 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(
         const bf16x8 ap = __builtin_bit_cast(bf16x8, pa[h2]);
         const bf16x8 as = __builtin_bit_cast(bf16x8, da[h2]);
         const int r0 = qt * 32 + h2 * 16;
-        bf16x8 bo[DT], bq[DT];
+        bf16x8 bo[DH], bq[DH];
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          bo[dt] = col_operand_c<RS>(dOs, r0, dt * 32, lane);
-          bq[dt] = col_operand_c<RS>(Qs, r0, dt * 32, lane);
+        for (int dt = 0; dt < DH; ++dt) {
+          bo[dt] = col_operand_c<RS>(dOs, r0, (role * DH + dt) * 32, lane);
+          bq[dt] = col_operand_c<RS>(Qs, r0, (role * DH + dt) * 32, lane);
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
+        for (int dt = 0; dt < DH; ++dt) {
           dv[dt] = mfma32(ap, bo[dt], dv[dt]);
           dk[dt] = mfma32(as, bq[dt], dk[dt]);
         }
       }
     };
-    // One straight-line body per case. The exponentials of one tile are
-    // scheduled between the MFMAs of the other (a wave issues VALU work while
-    // its MFMAs run): tile 0's under tile 1's dP, tile 1's under tile 0's
-    // second dV/dK step.
+    // One straight-line body per case: this wave's tile, then the swap.
     auto tiles = [&](auto masked) __attribute__((always_inline)) {
-      f32x16 s0, dp0, s1, dp1;
-      u32x4 pa0[2], da0[2], pa1[2], da1[2];
-      sdp(0, s0, dp0);
+      f32x16 s, dp;
+      u32x4 pa[2], da[2];  // [16-row step]
+      sdp(role, s, dp);
       __builtin_amdgcn_sched_barrier(0);
-      sdp(1, s1, dp1);
-      p_ds(masked, 0, s0, dp0, pa0, da0);
-#pragma unroll
-      for (int i = 0; i < KS; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);  // ten VALU
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      dvdk(0, pa0, da0);
-      p_ds(masked, 1, s1, dp1, pa1, da1);
-#pragma unroll
-      for (int i = 0; i < 2 * DT; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-        __builtin_amdgcn_sched_group_barrier(0x002, 10, 1);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      dvdk(1, pa1, da1);
-      __builtin_amdgcn_sched_barrier(0);
+      p_ds(masked, role, s, dp, pa, da);
+      u32x4* mine = xch + wave * 64 * 4;
+      mine[lane] = pa[0];
+      mine[64 + lane] = pa[1];
+      mine[128 + lane] = da[0];
+      mine[192 + lane] = da[1];
     };
     if (full)
       tiles(std::false_type{});
     else
       tiles(std::true_type{});
+    __syncthreads();  // both halves of every key group's P and dS are in LDS
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      // Tile qt's P and dS: written by wave kg + 4 qt.
+      const u32x4* src = xch + (kg + 4 * qt) * 64 * 4;
+      u32x4 pa[2], da[2];
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        pa[h2] = src[h2 * 64 + lane];
+        da[h2] = src[128 + h2 * 64 + lane];
+      }
+      dvdk(qt, pa, da);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     if (item + 1 < n_items) stage(buf ^ 1);
   }
 
-  // dK (times scale) and dV, bf16: lane holds d column, key rows wave*32 + (i/4)*8 + 4 hl + i%4.
+  // dK (times scale) and dV, bf16: lane holds d column, key rows kg*32 + (i/4)*8 + 4 hl + i%4.
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) {
-    const int d = dt * 32 + (lane & 31);
+  for (int dt = 0; dt < DH; ++dt) {
+    const int d = (role * DH + dt) * 32 + (lane & 31);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int kl = wave * 32 + (r >> 2) * 8 + hl * 4 + (r & 3);
+      const int kl = kg * 32 + (r >> 2) * 8 + hl * 4 + (r & 3);
       if (kl < nk) {
         const size_t off = ((size_t)(b * Hkv + g) * Nk + k0 + kl) * D + d;
         dK[off] = __builtin_bit_cast(uint16_t, (__bf16)(dk[dt][r] * scale));
@@ -579,7 +612,7 @@ hipError_t launch_bwd_d(const BwdArgs& a) {
   const int n_kb = (a.f.Nk + kBwdBK - 1) / kBwdBK;
   const long n_wg = (long)a.f.B * a.f.Hkv * n_kb;
   if (n_wg > 0) {
-    hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((unsigned)n_wg), dim3(kBwdThreads), 0, st, (const uint16_t*)a.f.q,
+    hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((unsigned)n_wg), dim3(kDkdvThreads), 0, st, (const uint16_t*)a.f.q,
                        (const uint16_t*)a.f.k, (const uint16_t*)a.f.v, (const uint16_t*)a.dout, a.f.lse, a.dsum,
                        (uint16_t*)a.dk, (uint16_t*)a.dv, a.f.Hq, a.f.Hkv, a.f.Nq, a.f.Nk, a.f.scale, sl2,
                        a.f.causal, n_kb);
