@@ -30,14 +30,17 @@
 //        half of d (32 keys x d/2 in registers), so that a wave fits in half
 //        of the SIMD's registers and one wave's softmax runs under the
 //        other's MFMAs.
-//  * bwd_dq_kernel: one workgroup (4 waves) per (batch, query head, 128-row
-//    block); each wave owns 32 rows, whose Q and dO stay in registers. S and
-//    dP are recomputed transposed, S^T = K Q^T and dP^T = V dO^T, 64 keys at
-//    a time (K and V through LDS, the next block in flight in registers): in
-//    that MFMA result each lane holds one query row, so LSE and D are one
-//    value per lane, and its 16 keys are the B operand of dQ^T += K^T dS^T
-//    once K is read in that key order. dQ^T (d x 32 rows per wave) stays in
-//    registers until the end.
+//  * bwd_dq_kernel: one workgroup (8 waves, two per SIMD) per (batch, query
+//    head, 128-row block). Waves w and w + 4 share 32 rows, whose Q and dO
+//    stay in registers. S and dP are recomputed transposed, S^T = K Q^T and
+//    dP^T = V dO^T, 64 keys at a time (K and V double-buffered in LDS, the
+//    block after next in flight in registers), wave w + 4 r taking keys
+//    32 r..32 r + 31 of each block: in that MFMA result each lane holds one
+//    query row, so LSE and D are one value per lane, and its 16 keys are the
+//    B operand of dQ^T += K^T dS^T once K is read in that key order. The pair
+//    swaps these bf16 operands through LDS, and each wave accumulates dQ^T
+//    over all 64 keys for its half of d (d/2 x 32 rows in registers until
+//    the end).
 //    Recomputing S and dP here costs two more products than adding each key
 //    block's dQ into an fp32 accumulator with atomics, but those adds
 //    (B Hq Nq d of them per 128 keys) are carried out memory-side at a rate
@@ -410,15 +413,16 @@ __global__ __launch_bounds__(kDkdvThreads) void bwd_dkdv_kernel(
 }
 
 template <int D>
-__global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(
+__global__ __launch_bounds__(kDkdvThreads) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dsum,
     uint16_t* __restrict__ dQ, int Hq, int Hkv, int Nq, int Nk, float scale, float sl2, int causal, int n_qb) {
   using L = BwdLayout<D>;
-  constexpr int RS = L::RS, KS = L::KS, DT = L::DT;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * kDqBK * RS];
-  uint16_t* Ks = lds;
-  uint16_t* Vs = lds + kDqBK * RS;
+  constexpr int RS = L::RS, KS = L::KS, DH = L::DT / 2;
+  // [buffer][K, V] tiles of 64 rows, then per wave 64 lanes x 32 bytes of dS^T
+  // operands for its partner.
+  __shared__ __attribute__((aligned(16))) uint16_t lds[4 * kDqBK * RS + 8 * 64 * 16];
+  u32x4* xch = reinterpret_cast<u32x4*>(lds + 4 * kDqBK * RS);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -436,9 +440,14 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(
   const int q0 = qb * kDqRows;
   const int diag = Nk - Nq;
 
+  // Waves w and w + 4 (one SIMD) share 32 rows: of each 64-key block, wave
+  // w + 4 r computes S^T, dP^T and dS^T for keys 32 r..32 r + 31; the pair
+  // swaps the bf16 dS^T operands through LDS, and each wave accumulates dQ^T
+  // over all 64 keys for one half of d (so that two waves share a SIMD).
   // This lane's query row, its Q and dO as the B operands of S^T = K Q^T and
   // dP^T = V dO^T (d = 16 ks + 8 (l/32) + 0..7), its LSE and D.
-  const int qw = q0 + wave * 32 + (lane & 31);
+  const int rg = wave & 3, role = wave >> 2;
+  const int qw = q0 + rg * 32 + (lane & 31);
   const bool qin = qw < Nq;
   const size_t qoff = ((size_t)bh * Nq + (qin ? qw : 0)) * D;
   bf16x8 qop[KS], dop[KS];
@@ -459,9 +468,9 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(
   }
   wait_vm_loads();
 
-  f32x16 dq[DT];
+  f32x16 dq[DH];
 #pragma unroll
-  for (int i = 0; i < DT; ++i) dq[i] = f32x16{};
+  for (int i = 0; i < DH; ++i) dq[i] = f32x16{};
 
   // Keys the block's last row sees: under the causal mask row i sees key j
   // iff j <= i + diag.
@@ -473,24 +482,32 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(
   const int n_kb = (kend + kDqBK - 1) / kDqBK;
   const uint16_t* Kh = K + (size_t)(b * Hkv + g) * Nk * D;
   const uint16_t* Vh = V + (size_t)(b * Hkv + g) * Nk * D;
-  RowsInFlight<D> kn, vn;
+  // K and V double-buffered in LDS: block j + 1 goes into the other buffer
+  // after block j's products, from registers loaded one block earlier.
+  RowsInFlight<D, kDkdvThreads> kn, vn;
+  auto load_block = [&](int j) __attribute__((always_inline)) {
+    const int first = j * kDqBK;
+    const int rows = Nk - first < kDqBK ? Nk - first : kDqBK;
+    kn.load(Kh + (size_t)first * D, rows, tid);
+    vn.load(Vh + (size_t)first * D, rows, tid);
+  };
+  auto store_block = [&](int buf) __attribute__((always_inline)) {
+    kn.store(lds + (2 * buf) * kDqBK * RS, tid);
+    vn.store(lds + (2 * buf + 1) * kDqBK * RS, tid);
+  };
   if (n_kb > 0) {
-    const int rows = Nk < kDqBK ? Nk : kDqBK;
-    kn.load(Kh, rows, tid);
-    vn.load(Vh, rows, tid);
+    load_block(0);
+    store_block(0);
+    if (n_kb > 1) load_block(1);
   }
 
   for (int j = 0; j < n_kb; ++j) {
     const int k0 = j * kDqBK;
-    __syncthreads();  // every wave is done with the previous block
-    kn.store(Ks, tid);
-    vn.store(Vs, tid);
-    if (j + 1 < n_kb) {
-      const int next = k0 + kDqBK;
-      const int rows = Nk - next < kDqBK ? Nk - next : kDqBK;
-      kn.load(Kh + (size_t)next * D, rows, tid);
-      vn.load(Vh + (size_t)next * D, rows, tid);
-    }
+    const int buf = j & 1;
+    const uint16_t* Ks = lds + (2 * buf) * kDqBK * RS;
+    const uint16_t* Vs = lds + (2 * buf + 1) * kDqBK * RS;
+    // Block j is in this buffer, every wave is done with the other one, and
+    // the previous block's dS^T swap has been read.
     __syncthreads();
 
     // Masks only at a ragged key block or where the causal diagonal crosses
@@ -537,58 +554,58 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(
     // dQ^T += K^T dS^T for one 32-key tile: A operand K read across key rows
     // in the order of the B operand's elements.
     auto dq_mm = [&](int kt, const u32x4* bs) __attribute__((always_inline)) {
-      bf16x8 ka[2][DT];
+      bf16x8 ka[2][DH];
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) ka[h2][dt] = col_operand_c<RS>(Ks, kt * 32 + h2 * 16, dt * 32, lane);
+        for (int dt = 0; dt < DH; ++dt)
+          ka[h2][dt] = col_operand_c<RS>(Ks, kt * 32 + h2 * 16, (role * DH + dt) * 32, lane);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
         const bf16x8 bsv = __builtin_bit_cast(bf16x8, bs[h2]);
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) dq[dt] = mfma32(ka[h2][dt], bsv, dq[dt]);
+        for (int dt = 0; dt < DH; ++dt) dq[dt] = mfma32(ka[h2][dt], bsv, dq[dt]);
       }
     };
-    // The exponentials of one tile are scheduled between the MFMAs of the
-    // other (a wave issues VALU work while its MFMAs run): tile 0's under
-    // tile 1's S^T and dP^T, tile 1's under tile 0's dQ^T product.
+    // One straight-line body per case: this wave's key tile, then the swap.
     auto tiles = [&](auto masked) __attribute__((always_inline)) {
-      f32x16 st0, dpt0, st1, dpt1;
-      u32x4 bs0[2], bs1[2];
-      sdp(0, st0, dpt0);
+      f32x16 st, dpt;
+      u32x4 bs[2];
+      sdp(role, st, dpt);
       __builtin_amdgcn_sched_barrier(0);
-      sdp(1, st1, dpt1);
-      ds_t(masked, 0, st0, dpt0, bs0);
-#pragma unroll
-      for (int i = 0; i < KS; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);  // ten VALU
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      dq_mm(0, bs0);
-      ds_t(masked, 1, st1, dpt1, bs1);
-#pragma unroll
-      for (int i = 0; i < 2 * DT; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-        __builtin_amdgcn_sched_group_barrier(0x002, 10, 1);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      dq_mm(1, bs1);
-      __builtin_amdgcn_sched_barrier(0);
+      ds_t(masked, role, st, dpt, bs);
+      u32x4* mine = xch + wave * 128;
+      mine[lane] = bs[0];
+      mine[64 + lane] = bs[1];
     };
     if (full)
       tiles(std::false_type{});
     else
       tiles(std::true_type{});
+    __syncthreads();  // both key tiles' dS^T of every row group are in LDS
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      // Key tile kt's dS^T: written by wave rg + 4 kt.
+      const u32x4* src = xch + (rg + 4 * kt) * 128;
+      u32x4 bs[2];
+      bs[0] = src[lane];
+      bs[1] = src[64 + lane];
+      dq_mm(kt, bs);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (j + 1 < n_kb) {
+      store_block(buf ^ 1);
+      if (j + 2 < n_kb) load_block(j + 2);
+    }
   }
 
   // dQ (times scale), bf16. C layout of dQ^T: lane l holds row qw, d columns
-  // dt*32 + 8 a + 4 hl + 0..3 (a = 0..3) in elements 4 a + 0..3.
+  // (role DH + dt)*32 + 8 a + 4 hl + 0..3 (a = 0..3) in elements 4 a + 0..3.
   if (qin) {
-    uint16_t* out = dQ + ((size_t)bh * Nq + qw) * D;
+    uint16_t* out = dQ + ((size_t)bh * Nq + qw) * D + role * DH * 32;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+    for (int dt = 0; dt < DH; ++dt)
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
         const u32x2 w = u32x2{pack_bf16x2(dq[dt][4 * a] * scale, dq[dt][4 * a + 1] * scale),
@@ -622,7 +639,7 @@ hipError_t launch_bwd_d(const BwdArgs& a) {
   const int n_qb = (a.f.Nq + kDqRows - 1) / kDqRows;
   const long n_wq = (long)a.f.B * a.f.Hq * n_qb;
   if (n_wq > 0) {
-    hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3((unsigned)n_wq), dim3(kBwdThreads), 0, st, (const uint16_t*)a.f.q,
+    hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3((unsigned)n_wq), dim3(kDkdvThreads), 0, st, (const uint16_t*)a.f.q,
                        (const uint16_t*)a.f.k, (const uint16_t*)a.f.v, (const uint16_t*)a.dout, a.f.lse, a.dsum,
                        (uint16_t*)a.dq, a.f.Hq, a.f.Hkv, a.f.Nq, a.f.Nk, a.f.scale, sl2, a.f.causal, n_qb);
   }
