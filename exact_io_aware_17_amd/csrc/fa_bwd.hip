@@ -59,8 +59,7 @@
 namespace fa {
 namespace {
 
-constexpr int kBwdThreads = 256;   // dQ kernel: 4 waves
-constexpr int kDkdvThreads = 512;  // dK/dV kernel: 8 waves, two per SIMD
+constexpr int kBwdThreads = 512;  // dK/dV and dQ kernels: 8 waves, two per SIMD
 constexpr int kBwdBQ = 64;    // dK/dV kernel: query rows per block
 constexpr int kBwdBK = 128;   // dK/dV kernel: keys per workgroup (32 per wave)
 constexpr int kDqRows = 128;  // dQ kernel: query rows per workgroup (32 per wave)
@@ -107,23 +106,23 @@ __device__ __forceinline__ bf16x8 row_operand(const uint16_t* tile, int r0, int 
 // rows zero) in two halves: global loads into registers (issued one block
 // ahead, so that their latency hides under the current block's work), then
 // the stores into the tile.
-template <int D, int NT = kBwdThreads>
+template <int D>
 struct RowsInFlight {
   static constexpr int CH = D / 8;
-  static constexpr int N = 64 * CH / NT;
+  static constexpr int N = 64 * CH / kBwdThreads;
   u32x4 r[N];
   __device__ __forceinline__ void load(const uint16_t* __restrict__ src, int nrows, int tid) {
     if (nrows == 64) {
 #pragma unroll
       for (int i = 0; i < N; ++i) {
-        const int id = tid + i * NT;
+        const int id = tid + i * kBwdThreads;
         r[i] = *reinterpret_cast<const u32x4*>(src + (size_t)(id / CH) * D + (id % CH) * 8);
       }
       return;
     }
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-      const int id = tid + i * NT;
+      const int id = tid + i * kBwdThreads;
       const int row = id / CH, ch = id % CH;
       r[i] = row < nrows ? *reinterpret_cast<const u32x4*>(src + (size_t)row * D + ch * 8) : u32x4{0u, 0u, 0u, 0u};
     }
@@ -131,7 +130,7 @@ struct RowsInFlight {
   __device__ __forceinline__ void store(uint16_t* tile, int tid) const {
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-      const int id = tid + i * NT;
+      const int id = tid + i * kBwdThreads;
       *reinterpret_cast<u32x4*>(tile + (id / CH) * BwdLayout<D>::RS + (id % CH) * 8) = r[i];
     }
   }
@@ -163,7 +162,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restric
 __device__ __forceinline__ void wait_vm_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 template <int D>
-__global__ __launch_bounds__(kDkdvThreads) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dsum,
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int Hq, int Hkv, int Nq, int Nk, float scale, float sl2,
@@ -216,7 +215,7 @@ __global__ __launch_bounds__(kDkdvThreads) void bwd_dkdv_kernel(
     if (kw < nk) kop[ks] = *reinterpret_cast<const bf16x8*>(Kh + (size_t)kw * D + ks * 16 + hl * 8);
   }
   {
-    RowsInFlight<D, kDkdvThreads> vr;
+    RowsInFlight<D> vr;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       vr.load(Vh + (size_t)h * 64 * D, nk - h * 64, tid);
@@ -240,7 +239,7 @@ __global__ __launch_bounds__(kDkdvThreads) void bwd_dkdv_kernel(
   // Work items: (query head of the group, query block), query block fastest.
   const int per_head = n_qb > qb0 ? n_qb - qb0 : 0;
   const int n_items = group * per_head;
-  RowsInFlight<D, kDkdvThreads> qn, don;
+  RowsInFlight<D> qn, don;
   float lse_n = kNegInf, d_n = 0.f;
   auto fetch = [&](int item) __attribute__((always_inline)) {
     const int hh = item / per_head, qb = qb0 + item % per_head;
@@ -413,7 +412,7 @@ __global__ __launch_bounds__(kDkdvThreads) void bwd_dkdv_kernel(
 }
 
 template <int D>
-__global__ __launch_bounds__(kDkdvThreads) void bwd_dq_kernel(
+__global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dsum,
     uint16_t* __restrict__ dQ, int Hq, int Hkv, int Nq, int Nk, float scale, float sl2, int causal, int n_qb) {
@@ -484,7 +483,7 @@ __global__ __launch_bounds__(kDkdvThreads) void bwd_dq_kernel(
   const uint16_t* Vh = V + (size_t)(b * Hkv + g) * Nk * D;
   // K and V double-buffered in LDS: block j + 1 goes into the other buffer
   // after block j's products, from registers loaded one block earlier.
-  RowsInFlight<D, kDkdvThreads> kn, vn;
+  RowsInFlight<D> kn, vn;
   auto load_block = [&](int j) __attribute__((always_inline)) {
     const int first = j * kDqBK;
     const int rows = Nk - first < kDqBK ? Nk - first : kDqBK;
@@ -629,7 +628,7 @@ hipError_t launch_bwd_d(const BwdArgs& a) {
   const int n_kb = (a.f.Nk + kBwdBK - 1) / kBwdBK;
   const long n_wg = (long)a.f.B * a.f.Hkv * n_kb;
   if (n_wg > 0) {
-    hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((unsigned)n_wg), dim3(kDkdvThreads), 0, st, (const uint16_t*)a.f.q,
+    hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((unsigned)n_wg), dim3(kBwdThreads), 0, st, (const uint16_t*)a.f.q,
                        (const uint16_t*)a.f.k, (const uint16_t*)a.f.v, (const uint16_t*)a.dout, a.f.lse, a.dsum,
                        (uint16_t*)a.dk, (uint16_t*)a.dv, a.f.Hq, a.f.Hkv, a.f.Nq, a.f.Nk, a.f.scale, sl2,
                        a.f.causal, n_kb);
@@ -639,7 +638,7 @@ hipError_t launch_bwd_d(const BwdArgs& a) {
   const int n_qb = (a.f.Nq + kDqRows - 1) / kDqRows;
   const long n_wq = (long)a.f.B * a.f.Hq * n_qb;
   if (n_wq > 0) {
-    hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3((unsigned)n_wq), dim3(kDkdvThreads), 0, st, (const uint16_t*)a.f.q,
+    hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3((unsigned)n_wq), dim3(kBwdThreads), 0, st, (const uint16_t*)a.f.q,
                        (const uint16_t*)a.f.k, (const uint16_t*)a.f.v, (const uint16_t*)a.dout, a.f.lse, a.dsum,
                        (uint16_t*)a.dq, a.f.Hq, a.f.Hkv, a.f.Nq, a.f.Nk, a.f.scale, sl2, a.f.causal, n_qb);
   }
