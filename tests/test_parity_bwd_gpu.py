@@ -67,6 +67,10 @@ CASES = [
     synth.Workload("bwd_one_query_one_key", 1, 1, 1, 1, 1, 128),
     synth.Workload("bwd_keys_below_one_block", 1, 2, 2, 150, 17, 128, seed=4),
     synth.Workload("bwd_gqa_8to1_d64_causal", 1, 8, 1, 130, 190, 64, causal=True, seed=6),
+    # Tails one row / one key past a block edge (the second wave of a pair
+    # then holds a single valid row or key), and a causal diagonal offset.
+    synth.Workload("bwd_gqa_4to1_d128_tail_129", 1, 8, 2, 129, 129, 128, seed=7),
+    synth.Workload("bwd_gqa_4to1_d128_causal_65x257", 2, 8, 2, 65, 257, 128, causal=True, seed=8),
 ]
 
 
