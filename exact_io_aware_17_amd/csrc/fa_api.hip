@@ -146,6 +146,8 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
     if (!workspace || workspace_bytes < total) return FA_ERR_WORKSPACE;
     if (((uintptr_t)workspace & 255u) != 0) return FA_ERR_ALIGN;
   }
+  // Grids: dK/dV kernel bwd_grid, D kernel B*Hq*Nq/4 (rounded up); the dQ
+  // kernel's B*Hq*ceil(Nq/128) is never larger than the D kernel's.
   if (fa::bwd_grid(B, Hkv, Nk) > kMaxGridX || (long long)B * Hq * Nq / 4 + 1 > kMaxGridX)
     return FA_ERR_UNSUPPORTED;
   if (nq == 0 && nkv == 0) return FA_OK;
