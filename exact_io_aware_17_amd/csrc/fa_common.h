@@ -184,9 +184,13 @@ __device__ __forceinline__ int score_key(int r0, int i, int lane) {
   return r0 + (i >> 3) * 16 + (lane >> 5) * 8 + (i & 7);
 }
 
+// Two floats rounded to bf16 (nearest even), a in the low half: one
+// v_cvt_pk_bf16_f32 (converting the halves separately and merging them costs
+// three more instructions).
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  __bf16 x = (__bf16)a, y = (__bf16)b;
-  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
 }
 
 }  // namespace fa
