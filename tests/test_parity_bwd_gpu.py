@@ -86,6 +86,31 @@ def test_bwd_full_oracle(w):
         assert np.all(got[0][:, :, : w.Nq - w.Nk] == 0.0), "rows without keys must get dQ = 0"
 
 
+def _random_shapes(n=24, seed=2026):
+    """Seeded mixed shapes: batch 1-2, 1-3 KV heads, GQA 1/2/4, 2..399 rows and
+    keys (at least two keys, so that no gradient is exactly zero), d 64 or
+    128, with and without causal."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        d = int(rng.choice([64, 128]))
+        hkv = int(rng.integers(1, 4))
+        hq = hkv * int(rng.choice([1, 2, 4]))
+        out.append(synth.Workload(f"bwd_random_{i}", int(rng.integers(1, 3)), hq, hkv, int(rng.integers(2, 400)),
+                                  int(rng.integers(2, 400)), d, causal=bool(rng.integers(0, 2)), seed=200 + i))
+    return out
+
+
+@pytest.mark.parametrize("w", _random_shapes(), ids=lambda w: w.name)
+def test_bwd_random_shapes(w):
+    say(f"case bwd random {w.name}: B{w.B} Hq{w.Hq} Hkv{w.Hkv} {w.Nq}x{w.Nk} d{w.d} causal={w.causal}")
+    got = _run(w)
+    q, k, v = synth.inputs_f64(w)
+    do = _f64(w.seed, synth.TENSOR_DO, w.q_shape)
+    dq, dk, dv, _ = oracle.attention_backward(q, k, v, do, w.scale, w.causal)
+    _check(got, (dq, dk, dv), w.name)
+
+
 @pytest.mark.parametrize("name", ["batched", "batched_causal", "pages_shape"])
 def test_bwd_full_size_heads(name):
     """Full-size launches: the batched shape (B4 H16 2048^2 d128), with and
