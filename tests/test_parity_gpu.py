@@ -58,6 +58,28 @@ def test_bf16_full_oracle(w):
     assert_close(errors(o, o_ref, lse, lse_ref), what=w.name)
 
 
+def _random_shapes(n=24, seed=2027):
+    """Seeded mixed shapes: batch 1-2, 1-3 KV heads, GQA 1/2/4, 1..399 rows and
+    keys, d 64, 128 or 256, with and without causal."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        d = int(rng.choice([64, 128, 256]))
+        hkv = int(rng.integers(1, 4))
+        hq = hkv * int(rng.choice([1, 2, 4]))
+        out.append(synth.Workload(f"fwd_random_{i}", int(rng.integers(1, 3)), hq, hkv, int(rng.integers(1, 400)),
+                                  int(rng.integers(1, 400)), d, causal=bool(rng.integers(0, 2)), seed=300 + i))
+    return out
+
+
+@pytest.mark.parametrize("w", _random_shapes(), ids=lambda w: w.name)
+def test_bf16_random_shapes(w):
+    say(f"case bf16 random {w.name}: B{w.B} Hq{w.Hq} Hkv{w.Hkv} {w.Nq}x{w.Nk} d{w.d} causal={w.causal}")
+    o, lse = _run_fwd(w)
+    o_ref, lse_ref = oracle_full(w)
+    assert_close(errors(o, o_ref, lse, lse_ref), what=w.name)
+
+
 @pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name)
 def test_fp32_full_oracle(w):
     say(f"case fp32 full {w.name}")
