@@ -95,6 +95,29 @@ def test_fp8_full_oracle(w):
     _check(o, lse, o_ref, lse_ref, _bound(q, k, v, w.scale, w.causal, o_ref), w.name)
 
 
+def _random_shapes(n=16, seed=2028):
+    """Seeded mixed shapes at d = 128: batch 1-2, 1-3 KV heads, GQA 1/2/4,
+    1..399 rows and keys, with and without causal."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        hkv = int(rng.integers(1, 4))
+        hq = hkv * int(rng.choice([1, 2, 4]))
+        out.append(synth.Workload(f"fp8_random_{i}", int(rng.integers(1, 3)), hq, hkv, int(rng.integers(1, 400)),
+                                  int(rng.integers(1, 400)), 128, causal=bool(rng.integers(0, 2)), seed=400 + i))
+    return out
+
+
+@pytest.mark.parametrize("w", _random_shapes(), ids=lambda w: w.name)
+def test_fp8_random_shapes(w):
+    say(f"case fp8 random {w.name}: B{w.B} Hq{w.Hq} Hkv{w.Hkv} {w.Nq}x{w.Nk} causal={w.causal}")
+    q8, k8, v8 = _inputs(w)
+    o, lse = _run(q8, k8, v8, w.scale, w.causal)
+    q, k, v = (oracle.e4m3_decode(t) * DS[i] for i, t in enumerate((q8, k8, v8)))
+    o_ref, lse_ref = oracle.attention(q, k, v, w.scale, w.causal)
+    _check(o, lse, o_ref, lse_ref, _bound(q, k, v, w.scale, w.causal, o_ref), w.name)
+
+
 def test_fp8_pages_shape_full_size_sampled():
     """The benchmark's launch (the pages' shape, B1 H8 4096x8192, E4M3), with
     the oracle computing sampled rows of three heads."""
