@@ -33,13 +33,14 @@
 //  * bwd_dq_kernel: one workgroup (8 waves, two per SIMD) per (batch, query
 //    head, 128-row block). Waves w and w + 4 share 32 rows, whose Q and dO
 //    stay in registers. S and dP are recomputed transposed, S^T = K Q^T and
-//    dP^T = V dO^T, 64 keys at a time (K and V double-buffered in LDS, the
-//    block after next in flight in registers), wave w + 4 r taking keys
-//    32 r..32 r + 31 of each block: in that MFMA result each lane holds one
+//    dP^T = V dO^T, 128 keys at a time (K double-buffered and V single-
+//    buffered in LDS, the block after next in flight in registers), wave
+//    w + 4 r taking the two 32-key tiles of keys 64 r..64 r + 63 of each
+//    block: in that MFMA result each lane holds one
 //    query row, so LSE and D are one value per lane, and its 16 keys are the
 //    B operand of dQ^T += K^T dS^T once K is read in that key order. The pair
 //    swaps these bf16 operands through LDS, and each wave accumulates dQ^T
-//    over all 64 keys for its half of d (d/2 x 32 rows in registers until
+//    over all 128 keys for its half of d (d/2 x 32 rows in registers until
 //    the end).
 //    Recomputing S and dP here costs two more products than adding each key
 //    block's dQ into an fp32 accumulator with atomics, but those adds
@@ -63,7 +64,7 @@ constexpr int kBwdThreads = 512;  // dK/dV and dQ kernels: 8 waves, two per SIMD
 constexpr int kBwdBQ = 64;    // dK/dV kernel: query rows per block
 constexpr int kBwdBK = 128;   // dK/dV kernel: keys per workgroup (32 per wave)
 constexpr int kDqRows = 128;  // dQ kernel: query rows per workgroup (32 per wave)
-constexpr int kDqBK = 64;     // dQ kernel: keys per block
+constexpr int kDqBK = 128;    // dQ kernel: keys per block (two 32-key tiles per wave)
 
 template <int D>
 struct BwdLayout {
@@ -418,10 +419,11 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(
     uint16_t* __restrict__ dQ, int Hq, int Hkv, int Nq, int Nk, float scale, float sl2, int causal, int n_qb) {
   using L = BwdLayout<D>;
   constexpr int RS = L::RS, KS = L::KS, DH = L::DT / 2;
-  // [buffer][K, V] tiles of 64 rows, then per wave 64 lanes x 32 bytes of dS^T
-  // operands for its partner.
-  __shared__ __attribute__((aligned(16))) uint16_t lds[4 * kDqBK * RS + 8 * 64 * 16];
-  u32x4* xch = reinterpret_cast<u32x4*>(lds + 4 * kDqBK * RS);
+  // Two K buffers and one V buffer of kDqBK rows, then per wave two tiles of
+  // 64 lanes x 32 bytes of dS^T operands for its partner.
+  constexpr int TB = kDqBK * RS;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[3 * TB + 8 * 256 * 8];
+  u32x4* xch = reinterpret_cast<u32x4*>(lds + 3 * TB);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -481,18 +483,25 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(
   const int n_kb = (kend + kDqBK - 1) / kDqBK;
   const uint16_t* Kh = K + (size_t)(b * Hkv + g) * Nk * D;
   const uint16_t* Vh = V + (size_t)(b * Hkv + g) * Nk * D;
-  // K and V double-buffered in LDS: block j + 1 goes into the other buffer
-  // after block j's products, from registers loaded one block earlier.
-  RowsInFlight<D> kn, vn;
+  // K double-buffered and V single-buffered in LDS: after the swap barrier of
+  // block j every wave is done with V(j) and with K(j - 1), so block j + 1
+  // goes in then, from registers loaded one block earlier.
+  RowsInFlight<D> kn[2], vn[2];
   auto load_block = [&](int j) __attribute__((always_inline)) {
-    const int first = j * kDqBK;
-    const int rows = Nk - first < kDqBK ? Nk - first : kDqBK;
-    kn.load(Kh + (size_t)first * D, rows, tid);
-    vn.load(Vh + (size_t)first * D, rows, tid);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int first = j * kDqBK + h * 64;
+      const int rows = Nk - first < 64 ? Nk - first : 64;
+      kn[h].load(Kh + (size_t)first * D, rows, tid);
+      vn[h].load(Vh + (size_t)first * D, rows, tid);
+    }
   };
-  auto store_block = [&](int buf) __attribute__((always_inline)) {
-    kn.store(lds + (2 * buf) * kDqBK * RS, tid);
-    vn.store(lds + (2 * buf + 1) * kDqBK * RS, tid);
+  auto store_block = [&](int kb_buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      kn[h].store(lds + kb_buf * TB + h * 64 * RS, tid);
+      vn[h].store(lds + 2 * TB + h * 64 * RS, tid);
+    }
   };
   if (n_kb > 0) {
     load_block(0);
@@ -503,10 +512,10 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(
   for (int j = 0; j < n_kb; ++j) {
     const int k0 = j * kDqBK;
     const int buf = j & 1;
-    const uint16_t* Ks = lds + (2 * buf) * kDqBK * RS;
-    const uint16_t* Vs = lds + (2 * buf + 1) * kDqBK * RS;
-    // Block j is in this buffer, every wave is done with the other one, and
-    // the previous block's dS^T swap has been read.
+    const uint16_t* Ks = lds + buf * TB;
+    const uint16_t* Vs = lds + 2 * TB;
+    // Block j's K and V are in LDS, and the previous block's dS^T swap has
+    // been read.
     __syncthreads();
 
     // Masks only at a ragged key block or where the causal diagonal crosses
@@ -567,35 +576,40 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(
         for (int dt = 0; dt < DH; ++dt) dq[dt] = mfma32(ka[h2][dt], bsv, dq[dt]);
       }
     };
-    // One straight-line body per case: this wave's key tile, then the swap.
+    // One straight-line body per case: this wave's two key tiles (keys
+    // 64 role .. 64 role + 63 of the block), then the swap.
     auto tiles = [&](auto masked) __attribute__((always_inline)) {
-      f32x16 st, dpt;
-      u32x4 bs[2];
-      sdp(role, st, dpt);
-      __builtin_amdgcn_sched_barrier(0);
-      ds_t(masked, role, st, dpt, bs);
-      u32x4* mine = xch + wave * 128;
-      mine[lane] = bs[0];
-      mine[64 + lane] = bs[1];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        f32x16 st, dpt;
+        u32x4 bs[2];
+        sdp(2 * role + tt, st, dpt);
+        __builtin_amdgcn_sched_barrier(0);
+        ds_t(masked, 2 * role + tt, st, dpt, bs);
+        u32x4* mine = xch + wave * 256 + tt * 128;
+        mine[lane] = bs[0];
+        mine[64 + lane] = bs[1];
+        __builtin_amdgcn_sched_barrier(0);
+      }
     };
     if (full)
       tiles(std::false_type{});
     else
       tiles(std::true_type{});
-    __syncthreads();  // both key tiles' dS^T of every row group are in LDS
+    __syncthreads();  // all four key tiles' dS^T of every row group are in LDS
+    if (j + 1 < n_kb) {
+      store_block(buf ^ 1);
+      if (j + 2 < n_kb) load_block(j + 2);
+    }
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      // Key tile kt's dS^T: written by wave rg + 4 kt.
-      const u32x4* src = xch + (rg + 4 * kt) * 128;
+    for (int kt = 0; kt < 4; ++kt) {
+      // Key tile kt's dS^T: written by wave rg + 4 (kt / 2), its tile kt % 2.
+      const u32x4* src = xch + (rg + 4 * (kt >> 1)) * 256 + (kt & 1) * 128;
       u32x4 bs[2];
       bs[0] = src[lane];
       bs[1] = src[64 + lane];
       dq_mm(kt, bs);
       __builtin_amdgcn_sched_barrier(0);
-    }
-    if (j + 1 < n_kb) {
-      store_block(buf ^ 1);
-      if (j + 2 < n_kb) load_block(j + 2);
     }
   }
 
