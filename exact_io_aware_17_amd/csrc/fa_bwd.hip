@@ -36,10 +36,10 @@
 //    dP^T = V dO^T, 128 keys at a time (K double-buffered and V single-
 //    buffered in LDS, the block after next in flight in registers), wave
 //    w + 4 r taking the two 32-key tiles of keys 64 r..64 r + 63 of each
-//    block: in that MFMA result each lane holds one
-//    query row, so LSE and D are one value per lane, and its 16 keys are the
-//    B operand of dQ^T += K^T dS^T once K is read in that key order. The pair
-//    swaps these bf16 operands through LDS, and each wave accumulates dQ^T
+//    block: in that MFMA result each lane holds one query row, so LSE and D
+//    are one value per lane, and its 16 keys are the B operand of
+//    dQ^T += K^T dS^T once K is read in that key order. The pair swaps these
+//    bf16 operands through LDS, and each wave accumulates dQ^T
 //    over all 128 keys for its half of d (d/2 x 32 rows in registers until
 //    the end).
 //    Recomputing S and dP here costs two more products than adding each key
