@@ -5,8 +5,8 @@ library's HIP kernels. torch supplies device memory and streams. If the library
 is not built, loading it raises; there is no fallback path.
 
 Entry points with the C names (tensors in, status checked, nothing returned):
-    fa_fwd, fa_fwd_fp32, fa_fwd_fp8, fa_bwd, fa_bwd_workspace_bytes, fa_fwd_splitkv, fa_fwd_splitkv_paged, fa_combine,
-    fa_splitkv_workspace_bytes, fa_status_str
+    fa_fwd, fa_fwd_fp32, fa_fwd_fp8, fa_bwd, fa_bwd_workspace_bytes, fa_fwd_splitkv, fa_fwd_splitkv_noalloc,
+    fa_fwd_splitkv_paged, fa_combine, fa_splitkv_workspace_bytes, fa_status_str
 Convenience wrappers that allocate the outputs:
     forward(q, k, v, causal=False, scale=None)            -> (o, lse)
     forward_fp32(q, k, v, causal=False, scale=None)       -> (o, lse)
@@ -38,6 +38,7 @@ SIGNATURES = {
     "fa_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P, _S, _P]),
     "fa_splitkv_workspace_bytes": (_S, [_I, _I, _I, _I, _I]),
     "fa_fwd_splitkv": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _P, _S, _P]),
+    "fa_fwd_splitkv_noalloc": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _P]),
     "fa_combine": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
     "fa_fwd_splitkv_paged": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _I, _I, _P, _S,
                                   _P]),
@@ -157,6 +158,22 @@ def fa_fwd_splitkv(q, k, v, o, lse, num_splits, workspace, scale=None, causal=Fa
                               _default_scale(d, scale), int(bool(causal)), int(num_splits), _ptr(workspace),
                               nbytes, _stream(stream))
     _check("fa_fwd_splitkv", st)
+
+
+# Size of the scratch fa_fwd_splitkv_noalloc uses (FA_NOALLOC_SCRATCH_BYTES in fa.h).
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def fa_fwd_splitkv_noalloc(q, k, v, o, lse, num_splits, scale=None, causal=False, stream=None):
+    """Split-KV forward with the library's own fixed scratch instead of a
+    workspace (for callers that cannot allocate); o, lse are the caller's."""
+    import torch
+    B, Hq, Hkv, Nq, Nk, d = _dims(q, k, v, torch.bfloat16)
+    _out_check(o, lse, q, torch.bfloat16)
+    st = lib().fa_fwd_splitkv_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Nq, Nk, d,
+                                      _default_scale(d, scale), int(bool(causal)), int(num_splits),
+                                      _stream(stream))
+    _check("fa_fwd_splitkv_noalloc", st)
 
 
 def fa_fwd_splitkv_paged(q, k_cache, v_cache, block_table, seq_lens, o, lse, num_splits, workspace, scale=None,

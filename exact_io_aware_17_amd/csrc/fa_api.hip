@@ -4,8 +4,17 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/fa.h"
 #include "fa_internal.h"
+
+// Scratch of fa_fwd_splitkv_noalloc: the split partials (O_s, then LSE_s)
+// live here instead of in a caller workspace. Each GPU holds its own copy
+// for the life of the process. Host code never uses the name `scratch` as a
+// device address (on the host it is only a stand-in for the symbol); the
+// device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) unsigned char scratch[FA_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -67,6 +76,43 @@ bool bwd_ws_sizes(int B, int Hq, int Nq, int d, size_t* total) {
   if (rows < 0 || rows > (1LL << 50)) return false;
   *total = round256((size_t)rows * 4u);  // fp32 D per row
   return true;
+}
+
+// Device address of `scratch` on device `dev`, looked up on the first call
+// for that device (with the device current) and cached.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+fa_status noalloc_scratch(void* stream, void** out) {
+  int dev = -1;
+  hipError_t e = stream ? hipStreamGetDevice((hipStream_t)stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return FA_ERR_LAUNCH;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) {
+      (void)hipGetLastError();
+      return FA_ERR_LAUNCH;
+    }
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) {
+      (void)hipGetLastError();
+      return FA_ERR_LAUNCH;
+    }
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) (void)hipSetDevice(cur);
+    if (e != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return FA_ERR_LAUNCH;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return FA_OK;
 }
 
 }  // namespace
@@ -182,6 +228,36 @@ fa_status fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, f
   if (rows == 0) return FA_OK;
   float* o_part = (float*)workspace;
   float* lse_part = (float*)((char*)workspace + ob);
+  fa::FwdArgs f{q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal, stream};
+  fa::SplitArgs sa{f, num_splits, o_part, lse_part};
+  st = launched(fa::launch_splitkv_partial(sa));
+  if (st != FA_OK) return st;
+  fa::CombineArgs ca{o_part, lse_part, o, lse, B, Hq, Nq, d, num_splits, stream};
+  return launched(fa::launch_combine(ca));
+}
+
+fa_status fa_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+                                 int Hkv, int Nq, int Nk, int d, float scale, int causal, int num_splits,
+                                 void* stream) {
+  fa_status st = check_common(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal);
+  if (st != FA_OK) return st;
+  if (d == 256) return FA_ERR_UNSUPPORTED;
+  if (num_splits < 1 || num_splits > kMaxSplits) return FA_ERR_ARG;
+  size_t ob = 0, total = 0;
+  if (!split_ws_sizes(B, Hq, Nq, d, num_splits, &ob, &total)) return FA_ERR_SHAPE;
+  if (total > (size_t)FA_NOALLOC_SCRATCH_BYTES) return FA_ERR_WORKSPACE;
+  if (fa::splitkv_grid(B, Hq, Hkv, Nq, num_splits) > kMaxGridX || B > kMaxGridYZ || Hkv > kMaxGridYZ)
+    return FA_ERR_UNSUPPORTED;
+  if (fa::combine_grid(B, Hq, Nq) > kMaxGridX) return FA_ERR_UNSUPPORTED;
+  if ((long long)B * Hq * Nq == 0) return FA_OK;
+  void* ws = nullptr;
+  st = noalloc_scratch(stream, &ws);
+  if (st != FA_OK) return st;
+  // The partial kernel writes every element of both partial arrays (an empty
+  // chunk writes O_s = 0 and LSE_s = -inf), so nothing left in the scratch by
+  // an earlier call is read.
+  float* o_part = (float*)ws;
+  float* lse_part = (float*)((char*)ws + ob);
   fa::FwdArgs f{q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal, stream};
   fa::SplitArgs sa{f, num_splits, o_part, lse_part};
   st = launched(fa::launch_splitkv_partial(sa));

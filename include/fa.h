@@ -170,6 +170,27 @@ fa_status fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, f
                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * fa_fwd_splitkv_noalloc -- fa_fwd_splitkv without a caller workspace, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  Same arguments,
+ * results (bit for bit: the same kernels run) and rules as fa_fwd_splitkv,
+ * minus the workspace.  The split partials go to a fixed scratch array of
+ * FA_NOALLOC_SCRATCH_BYTES bytes that the library holds on every GPU it runs
+ * on until the process ends; a call whose partials would not fit, i.e.
+ * fa_splitkv_workspace_bytes(B,Hq,Nq,d,num_splits) > FA_NOALLOC_SCRATCH_BYTES,
+ * returns FA_ERR_WORKSPACE and enqueues nothing.  The first call on a device
+ * looks the scratch up (hipGetSymbolAddress); no call allocates or frees.
+ * Every call on one GPU shares that GPU's scratch, which keeps the last call's
+ * contents: calls that overlap on one GPU (other streams, other host threads)
+ * race and must be serialized by the caller.  Nothing in the scratch needs
+ * clearing: each call writes every partial it reads.
+ */
+#define FA_NOALLOC_SCRATCH_BYTES (32u << 20)
+fa_status fa_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                                 int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                                 float scale, int causal, int num_splits, void* stream);
+
+/*
  * fa_fwd_splitkv_paged -- fa_fwd_splitkv over a paged K/V cache, one key
  * count per sequence.  PagedAttention appears on the "flash attention v3
  * paper" search-result page only as a name; the cache layout, table and

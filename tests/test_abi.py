@@ -29,7 +29,7 @@ def _declarations():
 def test_header_declarations_found():
     d = _declarations()
     assert set(d) == {"fa_fwd", "fa_fwd_fp32", "fa_fwd_fp8", "fa_bwd", "fa_bwd_workspace_bytes",
-                      "fa_splitkv_workspace_bytes", "fa_fwd_splitkv",
+                      "fa_splitkv_workspace_bytes", "fa_fwd_splitkv", "fa_fwd_splitkv_noalloc",
                       "fa_fwd_splitkv_paged", "fa_combine", "fa_status_str"}
 
 
@@ -162,6 +162,34 @@ def test_splitkv_argument_checks():
     assert _split(d=80) == 3
     assert _split(scale=-1.0) == 7
     assert _split(B=70000) == 3  # grid z limit
+
+
+def _noalloc(q=P, k=P, v=P, o=P, lse=P, B=2, Hq=8, Hkv=2, Nq=1, Nk=100, d=128, scale=0.1, causal=0, S=4):
+    return fa.lib().fa_fwd_splitkv_noalloc(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal, S, None)
+
+
+def test_noalloc_argument_checks():
+    """Every rejection happens on the host, before the scratch is looked up."""
+    assert _noalloc(S=0) == 7
+    assert _noalloc(S=1025) == 7
+    assert _noalloc(q=None) == 1
+    assert _noalloc(o=P + 8) == 4
+    assert _noalloc(Hq=7) == 2
+    assert _noalloc(d=80) == 3
+    assert _noalloc(d=256) == 3
+    assert _noalloc(scale=math.inf) == 7
+    # Partials beyond the fixed scratch: FA_ERR_WORKSPACE.
+    big = dict(B=64, Hq=32, Hkv=8, Nq=2, Nk=8192, S=16)
+    assert fa.fa_splitkv_workspace_bytes(64, 32, 2, 128, 16) > fa.NOALLOC_SCRATCH_BYTES
+    assert _noalloc(**big) == 5
+    assert fa.fa_splitkv_workspace_bytes(64, 32, 1, 128, 16) <= fa.NOALLOC_SCRATCH_BYTES
+
+
+def test_noalloc_scratch_size_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define FA_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m, "FA_NOALLOC_SCRATCH_BYTES not found"
+    assert int(m.group(1)) << int(m.group(2)) == fa.NOALLOC_SCRATCH_BYTES
 
 
 def _paged(q=P, kc=P, vc=P, bt=P, sl=P, o=P, lse=P, B=2, Hq=8, Hkv=2, Nq=1, d=128, num_pages=64, page=16,
