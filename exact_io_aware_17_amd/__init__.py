@@ -18,7 +18,6 @@ Convenience wrappers that allocate the outputs:
 from __future__ import annotations
 
 import ctypes
-import math
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -43,9 +42,13 @@ SIGNATURES = {
     "fa_fwd_splitkv_paged": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _I, _I, _P, _S,
                                   _P]),
     "fa_status_str": (ctypes.c_char_p, [_I]),
+    "fa_default_scale": (_F, [_I]),
+    "fa_build_hash": (ctypes.c_char_p, []),
 }
 
 _lib = None
+# The library must have been built from this source tree (fa_build_hash).
+VERIFY_BUILD = True
 
 
 class FaError(RuntimeError):
@@ -54,8 +57,12 @@ class FaError(RuntimeError):
         super().__init__(f"{fn} failed: {fa_status_str(status)}")
 
 
+class StaleLibraryError(RuntimeError):
+    """libfa.so was built from sources other than the ones in this tree."""
+
+
 def lib():
-    """Load libfa.so (raises if it has not been built)."""
+    """Load libfa.so (raises if it has not been built, or was built from other sources)."""
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
@@ -65,6 +72,12 @@ def lib():
             fn = getattr(handle, name)
             fn.restype = res
             fn.argtypes = args
+        if VERIFY_BUILD:
+            from .srchash import source_hash
+            built, tree = handle.fa_build_hash().decode(), source_hash()
+            if built != tree:
+                raise StaleLibraryError(f"{LIB_PATH} was built from sources {built}, the tree holds {tree}: "
+                                        "rebuild it with `python -m exact_io_aware_17_amd.build`")
         _lib = handle
     return _lib
 
@@ -113,11 +126,21 @@ def _dims(q, k, v, dtype):
 
 
 def _default_scale(d, scale):
-    return float(1.0 / math.sqrt(d)) if scale is None else float(scale)
+    """scale=None is argument defaulting: the library's own default for head size d."""
+    return float(lib().fa_default_scale(int(d))) if scale is None else float(scale)
+
+
+def _same_device(q, **tensors):
+    """Every tensor argument must live on q's GPU: the C ABI cannot tell a host
+    pointer from a device pointer, so a CPU tensor is refused here."""
+    for name, t in tensors.items():
+        if t is not None and t.device != q.device:
+            raise ValueError(f"{name} must be on {q.device}, got {t.device}")
 
 
 def _out_check(o, lse, q, odtype):
     import torch
+    _same_device(q, o=o, lse=lse)
     if o.dtype != odtype or tuple(o.shape) != tuple(q.shape) or not o.is_contiguous():
         raise ValueError("o must be a contiguous tensor shaped like q")
     if lse.dtype != torch.float32 or tuple(lse.shape) != tuple(q.shape[:3]) or not lse.is_contiguous():
@@ -153,6 +176,7 @@ def fa_fwd_splitkv(q, k, v, o, lse, num_splits, workspace, scale=None, causal=Fa
     import torch
     B, Hq, Hkv, Nq, Nk, d = _dims(q, k, v, torch.bfloat16)
     _out_check(o, lse, q, torch.bfloat16)
+    _same_device(q, workspace=workspace)
     nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = lib().fa_fwd_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Nq, Nk, d,
                               _default_scale(d, scale), int(bool(causal)), int(num_splits), _ptr(workspace),
@@ -196,6 +220,7 @@ def fa_fwd_splitkv_paged(q, k_cache, v_cache, block_table, seq_lens, o, lse, num
     if dk != d or block_table.dim() != 2 or block_table.shape[0] != B or tuple(seq_lens.shape) != (B,):
         raise ValueError("k_cache / block_table / seq_lens shapes disagree with q")
     _out_check(o, lse, q, torch.bfloat16)
+    _same_device(q, workspace=workspace)
     nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = lib().fa_fwd_splitkv_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens),
                                     _ptr(o), _ptr(lse), B, Hq, Hkv, Nq, d, num_pages, page_size,
@@ -216,6 +241,11 @@ def fa_combine(o_part, lse_part, o, lse, stream=None):
         raise ValueError("lse_part must be [B, Hq, S, Nq]")
     if o.dtype != torch.bfloat16 or tuple(o.shape) != (B, Hq, Nq, d) or tuple(lse.shape) != (B, Hq, Nq):
         raise ValueError("o must be bf16 [B, Hq, Nq, d] and lse [B, Hq, Nq]")
+    if lse.dtype != torch.float32 or not o.is_contiguous() or not lse.is_contiguous():
+        raise ValueError("o and lse must be contiguous; lse float32")
+    if o_part.device.type != "cuda":
+        raise ValueError("o_part must be on the GPU")
+    _same_device(o_part, lse_part=lse_part, o=o, lse=lse)
     st = lib().fa_combine(_ptr(o_part), _ptr(lse_part), _ptr(o), _ptr(lse), B, Hq, Nq, d, S, _stream(stream))
     _check("fa_combine", st)
 
@@ -236,10 +266,7 @@ def fa_fwd_fp8(q, k, v, o, lse, descale, scale=None, causal=False, stream=None):
     import torch
     q, k, v = _fp8_view(q, "q"), _fp8_view(k, "k"), _fp8_view(v, "v")
     B, Hq, Hkv, Nq, Nk, d = _dims(q, k, v, torch.uint8)
-    if o.dtype != torch.bfloat16 or tuple(o.shape) != tuple(q.shape) or not o.is_contiguous():
-        raise ValueError("o must be a contiguous bf16 tensor shaped like q")
-    if lse.dtype != torch.float32 or tuple(lse.shape) != tuple(q.shape[:3]) or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 [B, Hq, Nq] tensor")
+    _out_check(o, lse, q, torch.bfloat16)
     qd, kd, vd = (float(x) for x in descale)
     st = lib().fa_fwd_fp8(_ptr(q), _ptr(k), _ptr(v), qd, kd, vd, _ptr(o), _ptr(lse), B, Hq, Hkv, Nq, Nk, d,
                           _default_scale(d, scale), int(bool(causal)), _stream(stream))
@@ -262,6 +289,7 @@ def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, scale=None, causal=Fals
     """Backward into caller-provided dq (like q), dk, dv (like k) bf16 tensors."""
     import torch
     B, Hq, Hkv, Nq, Nk, d = _dims(q, k, v, torch.bfloat16)
+    _same_device(q, o=o, dout=dout, lse=lse, dq=dq, dk=dk, dv=dv, workspace=workspace)
     for name, t, like in (("o", o, q), ("dout", dout, q), ("dq", dq, q), ("dk", dk, k), ("dv", dv, k)):
         if t.dtype != torch.bfloat16 or tuple(t.shape) != tuple(like.shape) or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous bf16 tensor shaped like {'q' if like is q else 'k'}")

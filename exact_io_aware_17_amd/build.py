@@ -9,6 +9,12 @@ import shutil
 import subprocess
 import sys
 
+try:
+    from .srchash import source_hash
+except ImportError:  # run as a script
+    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    from exact_io_aware_17_amd.srchash import source_hash
+
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
@@ -32,10 +38,11 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False, extra_flags=None) -> str:
-    """Compile every HIP source for gfx950 and link libfa.so; returns its path."""
+    """Compile every HIP source for gfx950 and link libfa.so; returns its path.
+    The hash of the sources is compiled in (fa_build_hash)."""
     cc = hipcc()
     os.makedirs(BUILD_DIR, exist_ok=True)
-    flags = HIP_FLAGS + list(extra_flags or [])
+    flags = HIP_FLAGS + [f'-DFA_SOURCE_HASH="{source_hash()}"'] + list(extra_flags or [])
     procs = []
     objs = []
     for src in SOURCES:

@@ -119,6 +119,14 @@ fa_status noalloc_scratch(void* stream, void** out) {
 
 extern "C" {
 
+#ifndef FA_SOURCE_HASH
+#define FA_SOURCE_HASH "unknown"
+#endif
+
+const char* fa_build_hash(void) { return FA_SOURCE_HASH; }
+
+float fa_default_scale(int d) { return d >= 1 ? (float)(1.0 / sqrt((double)d)) : 0.f; }
+
 const char* fa_status_str(fa_status s) {
   switch (s) {
     case FA_OK: return "FA_OK";

@@ -441,10 +441,11 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(
   const int q0 = qb * kDqRows;
   const int diag = Nk - Nq;
 
-  // Waves w and w + 4 (one SIMD) share 32 rows: of each 64-key block, wave
-  // w + 4 r computes S^T, dP^T and dS^T for keys 32 r..32 r + 31; the pair
-  // swaps the bf16 dS^T operands through LDS, and each wave accumulates dQ^T
-  // over all 64 keys for one half of d (so that two waves share a SIMD).
+  // Waves w and w + 4 (one SIMD) share 32 rows: of each 128-key block, wave
+  // w + 4 r computes S^T, dP^T and dS^T for the two 32-key tiles of keys
+  // 64 r..64 r + 63; the pair swaps the bf16 dS^T operands through LDS, and
+  // each wave accumulates dQ^T over all 128 keys for one half of d (so that
+  // two waves share a SIMD).
   // This lane's query row, its Q and dO as the B operands of S^T = K Q^T and
   // dP^T = V dO^T (d = 16 ks + 8 (l/32) + 0..7), its LSE and D.
   const int rg = wave & 3, role = wave >> 2;

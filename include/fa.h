@@ -74,8 +74,12 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
 
 /*
  * fa_fwd_fp32 -- the same operation in fp32 throughout (debug / reference
- * path; plain FMA arithmetic, no matrix cores).  Same layout and rules as
- * fa_fwd with float tensors.
+ * path; plain FMA arithmetic, no matrix cores).  It computes the standard
+ * self-attention defined at the top of this file with the online softmax of
+ * the "v1 -- basic version" bullets of "Flash Attention on the 5090 in CUDA
+ * C++" taken one key at a time (running max m, running denominator l, O
+ * rescaled by exp(m_old - m_new) whenever m rises), with exact expf/logf.
+ * Same layout and rules as fa_fwd with float tensors; d = 64 or 128.
  */
 fa_status fa_fwd_fp32(const float* q, const float* k, const float* v, float* o, float* lse,
                       int B, int Hq, int Hkv, int Nq, int Nk, int d,
@@ -142,9 +146,13 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * fa_splitkv_workspace_bytes -- bytes of workspace fa_fwd_splitkv needs:
- * partial outputs O_s [B,Hq,S,Nq,d] fp32 followed (at the next 256-byte
- * boundary) by partial LSE_s [B,Hq,S,Nq] fp32.  Returns 0 for invalid sizes.
+ * fa_splitkv_workspace_bytes -- bytes of workspace fa_fwd_splitkv needs for
+ * its per-chunk partial results (the split of the keys into chunks whose
+ * partial softmax results are merged afterwards is the decode scheme the
+ * FlashDecoding++ snippet of the "flash attention v3 paper" search-result
+ * page refers to): partial outputs O_s [B,Hq,S,Nq,d] fp32 followed (at the
+ * next 256-byte boundary) by partial LSE_s [B,Hq,S,Nq] fp32.  Returns 0 for
+ * invalid sizes.
  */
 size_t fa_splitkv_workspace_bytes(int B, int Hq, int Nq, int d, int num_splits);
 
@@ -220,7 +228,11 @@ fa_status fa_fwd_splitkv_paged(const void* q, const void* k_cache, const void* v
                                void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * fa_combine -- LSE-weighted merge of per-chunk results.
+ * fa_combine -- LSE-weighted merge of per-chunk results.  Each chunk's
+ * (O_s, LSE_s) is a finished online-softmax state over its keys; merging the
+ * states is the rescale step of the "v1 -- basic version" bullets of "Flash
+ * Attention on the 5090 in CUDA C++" (scale the older sums by exp(m_old -
+ * m_new) when the running max rises, then add) applied to whole chunks.
  * o_part [B,Hq,S,Nq,d] fp32, lse_part [B,Hq,S,Nq] fp32 in; o [B,Hq,Nq,d] bf16
  * and lse [B,Hq,Nq] fp32 out.  With M = max_s LSE_s, w_s = exp(LSE_s - M):
  * O = sum_s w_s O_s / sum_s w_s, LSE = M + ln(sum_s w_s); rows whose chunks
@@ -231,6 +243,22 @@ fa_status fa_combine(const float* o_part, const float* lse_part, void* o, float*
 
 /* fa_status_str -- static, human-readable name of a status code. */
 const char* fa_status_str(fa_status s);
+
+/*
+ * fa_default_scale -- the score scale the "Flash Attention 2 algorithm"
+ * pseudocode of "Flash Attention on the 5090 in CUDA C++" uses, DIM**-0.5,
+ * for head size d, rounded to fp32 (0 for d < 1).  Callers that have no scale
+ * of their own pass this value as `scale`.
+ */
+float fa_default_scale(int d);
+
+/*
+ * fa_build_hash -- static string: the hash of the sources the library was
+ * built from (16 hex digits of SHA-256 over csrc/ and include/, as computed by
+ * the package's srchash module).  The Python binding refuses a library whose
+ * hash differs from its source tree.
+ */
+const char* fa_build_hash(void);
 
 #ifdef __cplusplus
 }

@@ -20,8 +20,9 @@ def _declarations():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     decls = {}
-    for m in re.finditer(r"^\s*(fa_status|size_t|const char\s*\*)\s*(fa_\w+)\s*\(([^)]*)\)\s*;", text, re.M | re.S):
-        params = [p.strip() for p in m.group(3).split(",") if p.strip()]
+    for m in re.finditer(r"^\s*(fa_status|size_t|float|const char\s*\*)\s*(fa_\w+)\s*\(([^)]*)\)\s*;", text,
+                         re.M | re.S):
+        params = [p.strip() for p in m.group(3).split(",") if p.strip() and p.strip() != "void"]
         decls[m.group(2)] = (m.group(1), len(params))
     return decls
 
@@ -30,7 +31,8 @@ def test_header_declarations_found():
     d = _declarations()
     assert set(d) == {"fa_fwd", "fa_fwd_fp32", "fa_fwd_fp8", "fa_bwd", "fa_bwd_workspace_bytes",
                       "fa_splitkv_workspace_bytes", "fa_fwd_splitkv", "fa_fwd_splitkv_noalloc",
-                      "fa_fwd_splitkv_paged", "fa_combine", "fa_status_str"}
+                      "fa_fwd_splitkv_paged", "fa_combine", "fa_status_str", "fa_default_scale",
+                      "fa_build_hash"}
 
 
 def test_library_exports_every_declared_symbol():
@@ -251,3 +253,44 @@ def test_product_path_does_not_import_oracle():
                 text = open(os.path.join(dirpath, fn)).read()
                 assert "import oracle" not in text and "from oracle" not in text, fn
                 assert "oracle/" not in text, fn
+
+
+def test_loaded_library_matches_source_tree():
+    """A libfa.so built from other sources is refused; the one loaded here was
+    built from this tree."""
+    from exact_io_aware_17_amd.srchash import source_hash
+    assert fa.lib().fa_build_hash().decode() == source_hash()
+
+
+def test_stale_library_is_refused(monkeypatch):
+    import exact_io_aware_17_amd.srchash as sh
+    monkeypatch.setattr(fa, "_lib", None)
+    monkeypatch.setattr(sh, "source_hash", lambda: "0123456789abcdef")
+    with pytest.raises(fa.StaleLibraryError):
+        fa.lib()
+    monkeypatch.setattr(fa, "_lib", None)
+
+
+def test_default_scale_is_the_pages_dim_power():
+    for d in (64, 128, 256, 1, 7):
+        assert fa.lib().fa_default_scale(d) == pytest.approx(d ** -0.5, rel=1e-7)
+        assert fa._default_scale(d, None) == float(__import__("numpy").float32(1.0 / math.sqrt(d)))
+    assert fa.lib().fa_default_scale(0) == 0.0
+
+
+def test_binding_refuses_host_tensors_before_any_launch():
+    """Outputs, workspaces and partials on the CPU are refused in Python: the C
+    ABI cannot tell a host pointer from a device pointer."""
+    import torch
+    dev = torch.device("meta")  # stands in for a GPU tensor without needing one
+    q = torch.empty(1, 2, 16, 128, dtype=torch.bfloat16, device=dev)
+    lse_cpu = torch.empty(1, 2, 16, dtype=torch.float32)
+    o_cpu = torch.empty(1, 2, 16, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="must be on"):
+        fa._out_check(o_cpu, torch.empty(1, 2, 16, dtype=torch.float32, device=dev), q, torch.bfloat16)
+    with pytest.raises(ValueError, match="must be on"):
+        fa._out_check(torch.empty_like(q), lse_cpu, q, torch.bfloat16)
+    with pytest.raises(ValueError, match="must be on"):
+        fa._same_device(q, workspace=torch.empty(256, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="GPU"):
+        fa.fa_combine(torch.empty(1, 2, 3, 16, 128), torch.empty(1, 2, 3, 16), o_cpu, lse_cpu)
