@@ -31,6 +31,11 @@ Parity status of each function (the pins live in tests/test_oracle.py):
                            definition with the same mask, the identities
                            sum_j dK_j = 0 and sum_j dV_j = sum_i dO_i, V = 1
                            giving dQ = dK = 0, D = rowsum(dO * O)).
+* ``attention_backward_head`` -- the per-head step of ``attention_backward``
+                           (same code path, so the pins above cover it); its
+                           P and dP are also pinned directly (rows of P sum to
+                           one, P equals softmax(S) from ``attention``'s LSE,
+                           dP equals dO V^T).
 * ``prob_weighted_abs`` -- pinned (V = 1 gives W = 1; identical keys give
                            Pmax = 1/Nk; one-hot selection gives Pmax ~ 1 and
                            W = |selected V row|; brute force on a tiny case).
@@ -44,5 +49,5 @@ from .attention import (  # noqa: F401
     split_bounds,
     splitkv_partials,
 )
-from .backward import attention_backward  # noqa: F401
+from .backward import attention_backward, attention_backward_head  # noqa: F401
 from .fp8 import attention_fp8, e4m3_decode, e4m3_value, prob_weighted_abs  # noqa: F401

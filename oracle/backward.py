@@ -31,6 +31,30 @@ from .attention import _check
 NEG_INF = -np.inf
 
 
+def attention_backward_head(q, k, v, do, scale, causal=False):
+    """One query head: q, do [Nq, d], k, v [Nk, d] (its KV head). Returns
+    (dQ [Nq,d], dK [Nk,d], dV [Nk,d], D [Nq], P [Nq,Nk], dP [Nq,Nk]), the
+    head's contributions to dK and dV before any GQA sum, and the exact
+    probabilities and dP = dO V^T they come from. All float64."""
+    Nq, Nk = q.shape[0], k.shape[0]
+    s = (q @ k.T) * scale
+    if causal:
+        last = np.arange(Nq) + (Nk - Nq)
+        s[np.arange(Nk)[None, :] > last[:, None]] = NEG_INF
+    m = s.max(axis=1) if Nk else np.full(Nq, NEG_INF)
+    alive = np.isfinite(m)
+    e = np.exp(s - np.where(alive, m, 0.0)[:, None])
+    p = np.zeros_like(e)
+    p[alive] = e[alive] / e[alive].sum(axis=1, keepdims=True)
+    dv = p.T @ do
+    dp = do @ v.T
+    dsum = (p * dp).sum(axis=1)
+    ds = p * (dp - dsum[:, None])
+    dq = ds @ k * scale
+    dk = ds.T @ q * scale
+    return dq, dk, dv, dsum, p, dp
+
+
 def attention_backward(q, k, v, do, scale, causal=False):
     """Gradients (dQ [B,Hq,Nq,d], dK [B,Hkv,Nk,d], dV [B,Hkv,Nk,d]) of the
     loss whose gradient with respect to O = attention(q, k, v) is `do`.
@@ -45,20 +69,10 @@ def attention_backward(q, k, v, do, scale, causal=False):
     for b in range(B):
         for h in range(Hq):
             g = h // group
-            s = (q[b, h] @ k[b, g].T) * scale
-            if causal:
-                last = np.arange(Nq) + (Nk - Nq)
-                s[np.arange(Nk)[None, :] > last[:, None]] = NEG_INF
-            m = s.max(axis=1) if Nk else np.full(Nq, NEG_INF)
-            alive = np.isfinite(m)
-            e = np.exp(s - np.where(alive, m, 0.0)[:, None])
-            p = np.zeros_like(e)
-            p[alive] = e[alive] / e[alive].sum(axis=1, keepdims=True)
-            dv[b, g] += p.T @ do[b, h]
-            dp = do[b, h] @ v[b, g].T
-            dsum = (p * dp).sum(axis=1)
-            ds = p * (dp - dsum[:, None])
-            dq[b, h] = ds @ k[b, g] * scale
-            dk[b, g] += ds.T @ q[b, h] * scale
+            dq_h, dk_h, dv_h, dsum, _, _ = attention_backward_head(q[b, h], k[b, g], v[b, g], do[b, h], scale,
+                                                                   causal)
+            dq[b, h] = dq_h
+            dk[b, g] += dk_h
+            dv[b, g] += dv_h
             dd[b, h] = dsum
     return dq, dk, dv, dd

@@ -66,11 +66,20 @@ def errors(o, o_ref, lse, lse_ref):
             "nan": bool(np.isnan(o).any() or np.isnan(lse).any())}
 
 
-def assert_close(err, o_tol=O_TOL, lse_tol=LSE_TOL, what=""):
+# Relative Frobenius error of O for bf16 inputs. Rounding P to bf16 for P.V and
+# O to bf16 each contribute about 2^-9/sqrt(3) ~ 1.1e-3 (measured 2-2.5e-3);
+# one 64-key tile dropped or read stale at Nk = 8192 moves O by about
+# sqrt(64 / 8192) ~ 9e-2 of its norm, far above this bound, while the absolute
+# O bound (2e-2) is about one standard deviation of |O| there.
+O_FRO_TOL = 1e-2
+
+
+def assert_close(err, o_tol=O_TOL, lse_tol=LSE_TOL, what="", o_fro_tol=O_FRO_TOL):
     say(f"  {what}: {err}")
     assert not err["nan"], f"{what}: NaN in output"
     assert err["o_max"] <= o_tol, f"{what}: max|O-O_ref| = {err['o_max']:.3e} > {o_tol}"
     assert err["lse_max"] <= lse_tol, f"{what}: max|LSE-LSE_ref| = {err['lse_max']:.3e} > {lse_tol}"
+    assert err["o_rel_fro"] <= o_fro_tol, f"{what}: ||O-O_ref||/||O_ref|| = {err['o_rel_fro']:.3e} > {o_fro_tol}"
 
 
 def sample_rows(nq, n_random=24, seed=0, tile=128):

@@ -94,3 +94,29 @@ def test_backward_row_without_keys():
     dq, dk, dv, dsum = oracle.attention_backward(q, k, v, do, 0.5, True)
     # Nq - Nk = 3: rows 0..2 see no key.
     assert np.all(dq[0, 0, :3] == 0.0) and np.all(dsum[0, 0, :3] == 0.0)
+
+
+def test_backward_head_intermediates():
+    """attention_backward_head's P and dP: rows of P sum to one (zero for rows
+    without keys), P = exp(S - LSE) with attention's LSE, dP = dO V^T, and the
+    head's gradients sum to attention_backward's under GQA."""
+    rng = np.random.default_rng(11)
+    Nq, Nk, d, scale = 7, 5, 6, 0.4
+    q, k, v, do = (rng.standard_normal(s) for s in ((Nq, d), (Nk, d), (Nk, d), (Nq, d)))
+    for causal in (False, True):
+        dq, dk, dv, D, P, dP = oracle.attention_backward_head(q, k, v, do, scale, causal)
+        o, lse = oracle.attention(q[None, None], k[None, None], v[None, None], scale, causal)
+        alive = np.isfinite(lse[0, 0])
+        assert np.allclose(P.sum(1)[alive], 1.0, atol=1e-14) and np.all(P[~alive] == 0.0)
+        s = q @ k.T * scale
+        visible = ~(causal & (np.arange(Nk)[None, :] > np.arange(Nq)[:, None] + (Nk - Nq)))
+        ref = np.where(visible & alive[:, None], np.exp(s - np.where(alive, lse[0, 0], 0.0)[:, None]), 0.0)
+        assert np.allclose(P, ref, rtol=1e-12, atol=0)
+        assert np.allclose(dP, do @ v.T, rtol=1e-13, atol=1e-13)
+        assert np.allclose(D, (do * o[0, 0]).sum(1), atol=1e-12)
+    # GQA: two query heads on one KV head.
+    q2, do2 = rng.standard_normal((1, 2, Nq, d)), rng.standard_normal((1, 2, Nq, d))
+    full = oracle.attention_backward(q2, k[None, None], v[None, None], do2, scale, True)
+    parts = [oracle.attention_backward_head(q2[0, h], k, v, do2[0, h], scale, True) for h in range(2)]
+    assert np.allclose(full[1][0, 0], parts[0][1] + parts[1][1], atol=1e-13)
+    assert np.allclose(full[2][0, 0], parts[0][2] + parts[1][2], atol=1e-13)

@@ -85,7 +85,7 @@ def test_fp32_full_oracle(w):
     say(f"case fp32 full {w.name}")
     o, lse = _run_fwd(w, fp32=True)
     o_ref, lse_ref = oracle_full(w, bf16=False)
-    assert_close(errors(o, o_ref, lse, lse_ref), F32_TOL, F32_TOL, what=w.name + " fp32")
+    assert_close(errors(o, o_ref, lse, lse_ref), F32_TOL, F32_TOL, what=w.name + " fp32", o_fro_tol=F32_TOL)
 
 
 D256 = [
@@ -127,23 +127,32 @@ def test_bf16_d256_full_size_sampled(name):
         assert_close(errors(o[b, h, rows], o_ref[n], lse[b, h, rows], lse_ref[n]), what=f"{w.name} head {h}")
 
 
-LARGE = ["batched_prefill_b4h16_n2048", "batched_prefill_b4h16_n2048_causal", "pages_shape_h8_q4096_kv8192",
-         "long_causal_h32_n16384"]
-
-
-@pytest.mark.parametrize("name", LARGE)
-def test_bf16_full_size_sampled(name):
-    """Full-size launch (the configuration the benchmark times); the oracle
-    computes sampled rows of sampled heads one by one."""
+@pytest.mark.parametrize("name", ["batched_prefill_b4h16_n2048", "batched_prefill_b4h16_n2048_causal",
+                                  "pages_shape_h8_q4096_kv8192"])
+def test_bf16_full_size_every_element(name):
+    """Full-size launch (the configuration the benchmark times), every element
+    of every head against the oracle."""
     w = W[name]
-    say(f"case bf16 full-size {name}")
+    say(f"case bf16 full-size {name}, every head")
     o, lse = _run_fwd(w)
-    heads = sorted({(0, 0), (w.B - 1, w.Hq - 1), (w.B // 2, w.Hq // 2)})
-    rows = sample_rows(w.Nq, seed=hash(name) % 1000)
+    o_ref, lse_ref = oracle_full(w)
+    for b in range(w.B):
+        for h in range(w.Hq):
+            assert_close(errors(o[b, h], o_ref[b, h], lse[b, h], lse_ref[b, h]), what=f"{name} ({b},{h})")
+    assert_close(errors(o, o_ref, lse, lse_ref), what=f"{name} all heads")
+
+
+def test_bf16_long_causal_whole_heads():
+    """The long causal workload (B1 H32 16384^2) at full size: four whole heads
+    (first, last and two between) against the oracle, every row."""
+    w = W["long_causal_h32_n16384"]
+    say("case bf16 full-size long causal, 4 whole heads")
+    o, lse = _run_fwd(w)
+    heads = [(0, 0), (0, 9), (0, 22), (0, 31)]
+    rows = np.arange(w.Nq)
     o_ref, lse_ref = oracle_sample(w, heads, rows)
-    got_o = np.stack([o[b, h][rows] for (b, h) in heads])
-    got_l = np.stack([lse[b, h][rows] for (b, h) in heads])
-    assert_close(errors(got_o, o_ref, got_l, lse_ref), what=name)
+    for n, (b, h) in enumerate(heads):
+        assert_close(errors(o[b, h], o_ref[n], lse[b, h], lse_ref[n]), what=f"long causal head {h}")
     assert np.isfinite(lse).all() and np.isfinite(o).all()
 
 
@@ -156,7 +165,8 @@ def test_fp32_batched_sampled():
     o_ref, lse_ref = oracle_sample(w, heads, rows, bf16=False)
     got_o = np.stack([o[b, h][rows] for (b, h) in heads])
     got_l = np.stack([lse[b, h][rows] for (b, h) in heads])
-    assert_close(errors(got_o, o_ref, got_l, lse_ref), F32_TOL, F32_TOL, what="fp32 batched causal")
+    assert_close(errors(got_o, o_ref, got_l, lse_ref), F32_TOL, F32_TOL, what="fp32 batched causal",
+                 o_fro_tol=F32_TOL)
 
 
 def _run_decode(w, fetch_partials=False):
