@@ -2,15 +2,21 @@
 
 Default run (N=1): the pages' benchmark shape (B=1, H=8, Nq=4096, Nk=8192,
 d=128, bf16, non-causal) through fa_fwd, W warm-up steps then exactly K timed
-steps; one JSON line on stdout. The line also carries the split-KV decode
-workload (B=64, Hq=32, Hkv=8, Nk=8192, 16 splits) timed the same way, the
-same decode over a paged K/V cache (16-key pages in a random order), the
-pages' shape again with OCP E4M3 inputs through fa_fwd_fp8 and at head
-size 256 through fa_fwd, the backward pass (fa_bwd) on the pages' shape, the
-roofline of the dominant kernel, and the CPU oracle timed on a bounded sample.
+steps; one JSON line on stdout. The line also carries, each timed the same
+way with its own roofline (HBM traffic from the committed counter summaries
+when their source hash matches) and a bounded CPU-oracle baseline:
+  - the other prefill workloads (single head 256^2 d64, batched B4 H16 2048^2
+    with and without the causal mask, long causal B1 H32 16384^2);
+  - the split-KV decode workload (B=64, Hq=32, Hkv=8, Nk=8192, 16 splits) and
+    the same decode over a paged K/V cache (16-key pages in a random order);
+  - the pages' shape with OCP E4M3 inputs (fa_fwd_fp8) and at head size 256;
+  - the backward pass (fa_bwd) on the pages' shape;
+and the machine: ROCm version and the shader clock rocm-smi reports while the
+pages' shape runs back to back.
 
-  python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--all]
-  python bench.py --only prefill|prefill_fp8|prefill_d256|backward|decode|decode_paged --steps 3   (short runs under a profiler)
+  python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu]
+  python bench.py --only prefill [--workload NAME] | prefill_fp8 | prefill_d256 | backward | decode | decode_paged
+                  --steps 3   (short runs under a profiler)
   python bench.py --copy-calib                       (plain copy of known size, for counter scaling)
 """
 from __future__ import annotations
@@ -38,7 +44,10 @@ PREFILL = "pages_shape_h8_q4096_kv8192"
 PREFILL_FP8 = "pages_shape_fp8_h8_q4096_kv8192"
 PREFILL_D256 = "pages_shape_d256_h8_q4096_kv8192"
 DECODE = "gqa_decode_b64_hq32_hkv8_kv8192"
-OTHER_PREFILL = ["batched_prefill_b4h16_n2048", "batched_prefill_b4h16_n2048_causal", "long_causal_h32_n16384"]
+# The other prefill workloads, each timed in the default line with its own
+# roofline and CPU baseline (the first is launch-bound: 8 workgroups).
+OTHER_PREFILL = ["single_head_n256_d64", "batched_prefill_b4h16_n2048", "batched_prefill_b4h16_n2048_causal",
+                 "long_causal_h32_n16384"]
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "exact_io_aware_17_amd", "csrc")
 
@@ -232,32 +241,140 @@ def bench_decode_paged(w, steps, warmup, device, page=PAGE, min_warm_s=0.2):
             "gbs": nbytes / (wall / steps) / 1e9, "kernel_gbs": nbytes / (ev_ms * 1e-3) / 1e9}
 
 
-def cpu_baseline(w, budget_s=15.0):
-    """The fp64 oracle on the host, head by head, until the budget is spent."""
-    import oracle
+def host_info():
+    """CPU model, BLAS library and the threads it uses (for the CPU baselines)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
+    blas, threads = "unknown", len(os.sched_getaffinity(0))
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if info:
+            blas = f"{info[0].get('internal_api', '?')} {info[0].get('version', '')}".strip()
+            threads = max(i.get("num_threads", 1) for i in info)
     except Exception:  # pragma: no cover
-        threads = len(os.sched_getaffinity(0))
+        pass
+    return {"cpu_model": model, "blas": blas, "cores": threads}
+
+
+def _visible_keys(w, rows):
+    """Keys each query row sees (the bottom-right causal reading)."""
+    rows = np.asarray(rows, dtype=np.int64)
+    if not w.causal:
+        return np.full(rows.shape, w.Nk, dtype=np.int64)
+    return np.clip(rows + 1 + (w.Nk - w.Nq), 0, w.Nk)
+
+
+def cpu_baseline(w, budget_s=15.0, row_block=1024):
+    """The fp64 oracle on the host over a bounded sample of the workload: (batch,
+    head) slabs in order, each in blocks of query rows, until the budget is
+    spent. Prefill reports TFLOP/s (the FLOPs of the rows done); decode reports
+    GB/s (the algorithmic bytes of the slabs done, as for the GPU line)."""
+    import oracle
     group = w.Hq // w.Hkv
-    done = 0
-    t_total = 0.0
+    t_total, flops, rows_done, slabs = 0.0, 0.0, 0, 0
     for b in range(w.B):
         for h in range(w.Hq):
-            q, k, v = synth.inputs_f64(w, q_heads=[(b, h)], kv_heads=[(b, h // group)])
-            t0 = time.perf_counter()
-            oracle.attention(q[:, None], k[:, None], v[:, None], w.scale, w.causal)
-            t_total += time.perf_counter() - t0
-            done += 1
+            for r0 in range(0, w.Nq, row_block):
+                rows = np.arange(r0, min(w.Nq, r0 + row_block))
+                q, k, v = synth.inputs_f64(w, q_heads=[(b, h)], kv_heads=[(b, h // group)], q_rows=rows)
+                t0 = time.perf_counter()
+                oracle.attention(q[:, None], k[:, None], v[:, None], w.scale, w.causal, q_index=rows, nq=w.Nq)
+                t_total += time.perf_counter() - t0
+                flops += 4.0 * w.d * float(_visible_keys(w, rows).sum())
+                rows_done += len(rows)
+                if t_total >= budget_s:
+                    break
+            slabs += 1
             if t_total >= budget_s:
                 break
         if t_total >= budget_s:
             break
-    flops = w.flops() * done / (w.B * w.Hq)
-    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{done} of {w.B * w.Hq} (batch, head) slabs of {w.name}, all {w.Nq} query rows, "
-                      f"{t_total:.1f} s of fp64 numpy on the host"}
+    out = host_info()
+    frac = rows_done / max(w.B * w.Hq * w.Nq, 1)
+    sample = (f"{rows_done} of {w.B * w.Hq * w.Nq} query rows ({slabs} (batch, head) slabs) of {w.name}, "
+              f"{t_total:.1f} s of fp64 numpy on the host")
+    if w.num_splits:
+        return {"value": w.algorithmic_bytes() * frac / t_total / 1e9, "unit": "GB/s",
+                "cores": out["cores"], "kind": "oracle", "sample": sample,
+                "cpu_model": out["cpu_model"], "blas": out["blas"]}
+    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": out["cores"], "kind": "oracle",
+            "sample": sample, "cpu_model": out["cpu_model"], "blas": out["blas"]}
+
+
+def rocm_version():
+    for path in ("/opt/rocm/.info/version", "/opt/rocm/.info/version-dev"):
+        try:
+            with open(path) as f:
+                return f.read().strip()
+        except OSError:
+            continue
+    return None
+
+
+def _read_sclk_mhz():
+    """Current shader clock(s) in MHz from rocm-smi (a child process)."""
+    import subprocess
+    for exe in ("rocm-smi", "/opt/rocm/bin/rocm-smi"):
+        try:
+            out = subprocess.run([exe, "--showclocks", "--json"], capture_output=True, text=True, timeout=20).stdout
+        except (OSError, subprocess.TimeoutExpired):
+            continue
+        try:
+            data = json.loads(out)
+        except ValueError:
+            continue
+        vals = []
+        for card in data.values():
+            if isinstance(card, dict):
+                for key, val in card.items():
+                    if "sclk" in key.lower() and "speed" in key.lower():
+                        m = re.search(r"(\d+)\s*Mhz", str(val), re.I)
+                        if m:
+                            vals.append(int(m.group(1)))
+        if vals:
+            return vals
+    return None
+
+
+def sustained_sclk(step, seconds=2.0):
+    """Shader clock while `step` runs back to back for `seconds`: rocm-smi is
+    polled from a thread; returns the median, min and max MHz it reported."""
+    import threading
+    import torch
+    readings, stop = [], threading.Event()
+
+    def poll():
+        while not stop.is_set():
+            v = _read_sclk_mhz()
+            if v is None:
+                return
+            readings.extend(v)
+
+    th = threading.Thread(target=poll, daemon=True)
+    t_end = time.perf_counter() + seconds
+    for _ in range(20):
+        step()
+    torch.cuda.synchronize()
+    th.start()
+    while time.perf_counter() < t_end:
+        for _ in range(20):
+            step()
+        torch.cuda.synchronize()
+    stop.set()
+    th.join(timeout=30)
+    if not readings:
+        return {"sclk_mhz": None, "how": "rocm-smi --showclocks gave no reading"}
+    r = sorted(readings)
+    return {"sclk_mhz": r[len(r) // 2], "sclk_mhz_min": r[0], "sclk_mhz_max": r[-1], "readings": len(r),
+            "how": f"rocm-smi --showclocks polled while the pages' shape prefill ran back to back for {seconds} s"}
 
 
 def copy_calib(device, nbytes=1 << 30, steps=3):
@@ -278,9 +395,11 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--all", action="store_true", help="also time the other prefill workloads")
+    ap.add_argument("--all", action="store_true", help="(kept for old command lines; the other prefill "
+                                                          "workloads are always timed)")
     ap.add_argument("--only", choices=["prefill", "prefill_fp8", "prefill_d256", "backward", "decode", "decode_paged"],
                     default=None)
+    ap.add_argument("--workload", default=None, help="with --only prefill: the prefill workload (synth name)")
     ap.add_argument("--copy-calib", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -302,8 +421,9 @@ def main():
     wp = synth.WORKLOADS[PREFILL]
     wd = synth.WORKLOADS[DECODE]
     if args.only == "prefill":
-        r = bench_prefill(wp, args.steps, args.warmup, device, min_warm_s=0.0)
-        print(json.dumps({"only": "prefill", **r}))
+        w = synth.WORKLOADS[args.workload] if args.workload else wp
+        r = bench_prefill(w, args.steps, args.warmup, device, min_warm_s=0.0)
+        print(json.dumps({"only": "prefill", "workload": w.name, **r}))
         return
     if args.only == "backward":
         r = bench_backward(wp, args.steps, args.warmup, device, min_warm_s=0.0)
@@ -348,15 +468,28 @@ def main():
     rdp = bench_decode_paged(wd, args.steps, args.warmup, device)
     log(f"  {rdp}")
     others = {}
-    if args.all:
-        for name in OTHER_PREFILL:
-            w = synth.WORKLOADS[name]
-            log(f"prefill {name}")
-            r = bench_prefill(w, args.steps, args.warmup, device)
-            others[name] = {"tflops": round(r["tflops"], 2), "kernel_tflops": round(r["kernel_tflops"], 2),
-                            "kernel_ms": round(r["kernel_ms"], 4),
-                            "pct_peak": round(100 * r["kernel_tflops"] / PEAK_BF16_TFLOPS, 2)}
-            log(f"  {others[name]}")
+    for name in OTHER_PREFILL:
+        w = synth.WORKLOADS[name]
+        log(f"prefill {name}: warmup {args.warmup}, steps {args.steps}")
+        r = bench_prefill(w, args.steps, args.warmup, device)
+        log(f"  {r}")
+        others[name] = {
+            "workload": name, "B": w.B, "H": w.Hq, "Nq": w.Nq, "Nk": w.Nk, "d": w.d, "causal": w.causal,
+            "metric": "attention fwd TFLOPS (4*B*H*Nq*Nk*d per forward, halved under the causal mask)",
+            "value": round(r["tflops"], 2), "unit": "TFLOP/s", "ms_per_step": round(r["ms_per_step"], 5),
+            "roofline": {"bound": "mfma", "achieved": round(r["kernel_tflops"], 2), "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(r["kernel_tflops"] / PEAK_BF16_TFLOPS, 4),
+                         "traffic": traffic_from_profile(f"fwd_bf16_{name}_traffic.md", FWD_SOURCES),
+                         "kernel_ms": round(r["kernel_ms"], 5),
+                         "kernel": "fwd_bf16_kernel<64>" if w.d == 64 else "fwd_bf16_kernel<128>"}}
+    log("sustained shader clock ...")
+    wsc = synth.WORKLOADS[PREFILL]
+    import exact_io_aware_17_amd as fa
+    q_, k_, v_ = device_inputs(wsc, device)
+    o_, l_ = torch.empty_like(q_), torch.empty(q_.shape[:3], dtype=torch.float32, device=device)
+    clock = sustained_sclk(lambda: fa.fa_fwd(q_, k_, v_, o_, l_, scale=wsc.scale))
+    del q_, k_, v_, o_, l_
+    log(f"  {clock}")
 
     fwd_traffic = traffic_from_profile("fwd_bf16_pages_shape_traffic.md", FWD_SOURCES)
     fwd8_traffic = traffic_from_profile("fwd_fp8_pages_shape_traffic.md", FWD8_SOURCES)
@@ -423,12 +556,19 @@ def main():
                                       "kernel_ms": round(rdp["kernel_ms"], 5),
                                       "kernel": "splitkv_partial_kernel<128, true> + combine_kernel<128>"}},
     }
-    if others:
-        line["other_prefill"] = others
+    line["other_prefill"] = others
+    line["machine"] = {"rocm": rocm_version(), "gpu": torch.cuda.get_device_name(0), **clock,
+                       "peak_note": "frac is against the published peaks (2.5 PFLOP/s dense bf16 at 2.4 GHz, "
+                                    "5.0 fp8, 8 TB/s HBM)"}
     if not args.no_cpu:
         log("cpu baseline (oracle) ...")
-        line["cpu_baseline"] = cpu_baseline(wp)
+        line["cpu_baseline"] = cpu_baseline(wp, budget_s=8.0)
         log(f"  {line['cpu_baseline']}")
+        for name in OTHER_PREFILL:
+            others[name]["cpu_baseline"] = cpu_baseline(synth.WORKLOADS[name], budget_s=3.0)
+            log(f"  {name}: {others[name]['cpu_baseline']}")
+        line["decode"]["cpu_baseline"] = cpu_baseline(wd, budget_s=3.0)
+        log(f"  decode: {line['decode']['cpu_baseline']}")
     print(json.dumps(line), flush=True)
 
 

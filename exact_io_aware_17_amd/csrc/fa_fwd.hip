@@ -42,8 +42,10 @@
 //    wave skips the math of tiles its rows cannot see; only tiles that cross
 //    the diagonal or the ragged end are masked element-wise.
 //  * Workgroups are renumbered so that the query blocks of one head run on one
-//    XCD (its L2 then serves that head's K/V to all of them); under the causal
-//    mask the longest query blocks are issued first.
+//    XCD (its L2 then serves that head's K/V to all of them). Under the causal
+//    mask a workgroup takes the pair of query blocks n - 1 - p and p, so that
+//    all workgroups have the same work (a lone block p would see 2 (p + 1) key
+//    tiles).
 #include <type_traits>
 
 #include "fa_common.h"
@@ -98,7 +100,11 @@ __device__ __forceinline__ void tile_to_lds(uint32_t slot_lds, const uint16_t* s
   }
 }
 
-template <int D>
+// PAIRED (causal only): each workgroup takes query blocks n_qt - 1 - p and p of
+// one head, one after the other, so that every workgroup has the same number
+// of visible key tiles (2 (n_qt + 1) per pair) instead of 2 (qt + 1) for
+// block qt alone.
+template <int D, bool PAIRED>
 __global__ __launch_bounds__(kFwdThreads) void fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int Hq, int Hkv, int Nq, int Nk, float sl2, int causal,
@@ -118,9 +124,9 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_bf16_kernel(
 
   int wg = blockIdx.x;
   if ((n_wg & 7) == 0) wg = (wg & 7) * (n_wg >> 3) + (wg >> 3);
-  const int bh = wg / n_qt;
-  int qt = wg - bh * n_qt;
-  if (causal) qt = n_qt - 1 - qt;
+
+  // One query block: everything from here to the store of O and LSE.
+  auto item = [&](const int bh, const int qt) __attribute__((always_inline)) {
   const int b = bh / Hq, h = bh - b * Hq;
   const int g = h / (Hq / Hkv);
   const uint16_t* Qh = Q + (size_t)bh * Nq * D;
@@ -415,15 +421,42 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_bf16_kernel(
       if (lane < 32) LSE[(size_t)bh * Nq + qrow] = lsum > 0.f ? (M + fast_log2(lsum)) * kLn2 : kNegInf;
     }
   }
+  };
+
+  if constexpr (!PAIRED) {
+    const int bh = wg / n_qt;
+    const int qt = wg - bh * n_qt;
+    // Under the causal mask the longest query blocks go first.
+    item(bh, causal ? n_qt - 1 - qt : qt);
+  } else {
+    const int n_pairs = (n_qt + 1) / 2;
+    const int bh = wg / n_pairs;
+    const int p = wg - bh * n_pairs;
+    item(bh, n_qt - 1 - p);
+    if (p != n_qt - 1 - p) {
+      // The merge area and the tile slots of the first block are reused.
+      __syncthreads();
+      item(bh, p);
+    }
+  }
 }
 
 template <int D>
 hipError_t launch_fwd_bf16_d(const FwdArgs& a) {
   const int n_qt = (a.Nq + kFwdBM - 1) / kFwdBM;
+  const float sl2 = a.scale * kLog2e;
+  // Causal with at least two query blocks per head: paired blocks.
+  if (a.causal && n_qt >= 2) {
+    const long n_wg = (long)a.B * a.Hq * ((n_qt + 1) / 2);
+    if (n_wg == 0) return hipSuccess;
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, true>), dim3((unsigned)n_wg), dim3(kFwdThreads), 0,
+                       (hipStream_t)a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                       (uint16_t*)a.o, a.lse, a.Hq, a.Hkv, a.Nq, a.Nk, sl2, a.causal, n_qt, (int)n_wg);
+    return hipGetLastError();
+  }
   const long n_wg = (long)a.B * a.Hq * n_qt;
   if (n_wg == 0) return hipSuccess;
-  const float sl2 = a.scale * kLog2e;
-  hipLaunchKernelGGL(fwd_bf16_kernel<D>, dim3((unsigned)n_wg), dim3(kFwdThreads), 0, (hipStream_t)a.stream,
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, false>), dim3((unsigned)n_wg), dim3(kFwdThreads), 0, (hipStream_t)a.stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse,
                      a.Hq, a.Hkv, a.Nq, a.Nk, sl2, a.causal, n_qt, (int)n_wg);
   return hipGetLastError();
