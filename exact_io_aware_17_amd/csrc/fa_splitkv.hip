@@ -153,19 +153,33 @@ __global__ __launch_bounds__(kSplitThreads, 2) void splitkv_partial_kernel(
     src = Rows{K + (size_t)(b * Hkv + g) * Nk * D, V + (size_t)(b * Hkv + g) * Nk * D};
   }
   // Physical pages of the block starting at key kb (unused when contiguous).
+  // The wave keeps a window of 64 consecutive table entries in one register
+  // (lane j: logical page win + j, already clamped into [0, num_pages)), read
+  // with one vector load, so the loop reads page numbers with v_readlane
+  // instead of waiting on memory; the window moves only when a block needs a
+  // page past it (chunks longer than 64 pages).
+  int win = 0, tbl = 0;
+  auto load_window = [&](int lp) __attribute__((always_inline)) {
+    if constexpr (PAGED) {
+      win = lp;
+      const int l = lp + lane < max_pages ? lp + lane : max_pages - 1;
+      const int p = bt[l];
+      tbl = p < 0 ? 0 : (p < num_pages ? p : num_pages - 1);
+    }
+  };
   auto pages_of = [&](int kb, int (&pg)[3]) __attribute__((always_inline)) {
     if constexpr (PAGED) {
       const int lp = kb >> log2_page;
+      if (lp - win + 2 >= 64) load_window(lp);
 #pragma unroll
-      for (int j = 0; j < 3; ++j) {
-        const int l = lp + j < max_pages ? lp + j : max_pages - 1;
-        const int p = bt[l];
-        pg[j] = p < 0 ? 0 : (p < num_pages ? p : num_pages - 1);
-      }
+      for (int j = 0; j < 3; ++j) pg[j] = __builtin_amdgcn_readlane(tbl, lp - win + j);
     } else {
       pg[0] = pg[1] = pg[2] = 0;
     }
   };
+  if constexpr (PAGED) {
+    if (max_pages > 0) load_window(k0 >> log2_page);
+  }
   uint16_t* vw = vlds[wave];
   const char* vw_c = reinterpret_cast<const char*>(vw);
 
