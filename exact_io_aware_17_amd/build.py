@@ -19,6 +19,10 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libfa.so")
+# Debug build: every tile copy first fills its LDS destination with NaN
+# (FA_LDS_POISON), so that a read racing a copy shows up as NaN in O.
+POISON_BUILD_DIR = os.path.join(HERE, "_build_poison")
+POISON_LIB_PATH = os.path.join(HERE, "libfa_poison.so")
 SOURCES = ["fa_api.hip", "fa_fwd.hip", "fa_fwd_d256.hip", "fa_fwd_fp8.hip", "fa_fp32.hip", "fa_splitkv.hip", "fa_bwd.hip"]
 ARCH = "gfx950"
 
@@ -37,16 +41,19 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build the library)")
 
 
-def build(verbose: bool = False, extra_flags=None) -> str:
-    """Compile every HIP source for gfx950 and link libfa.so; returns its path.
-    The hash of the sources is compiled in (fa_build_hash)."""
+def build(verbose: bool = False, extra_flags=None, poison: bool = False) -> str:
+    """Compile every HIP source for gfx950 and link libfa.so (or, with
+    poison=True, the LDS-poisoning debug library libfa_poison.so); returns its
+    path. The hash of the sources is compiled in (fa_build_hash)."""
     cc = hipcc()
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    flags = HIP_FLAGS + [f'-DFA_SOURCE_HASH="{source_hash()}"'] + list(extra_flags or [])
+    build_dir, lib_path = (POISON_BUILD_DIR, POISON_LIB_PATH) if poison else (BUILD_DIR, LIB_PATH)
+    os.makedirs(build_dir, exist_ok=True)
+    flags = HIP_FLAGS + [f'-DFA_SOURCE_HASH="{source_hash()}"'] + (["-DFA_LDS_POISON"] if poison else [])
+    flags += list(extra_flags or [])
     procs = []
     objs = []
     for src in SOURCES:
-        obj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))
+        obj = os.path.join(build_dir, src.replace(".hip", ".o"))
         objs.append(obj)
         cmd = [cc, *flags, "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
@@ -64,14 +71,15 @@ def build(verbose: bool = False, extra_flags=None) -> str:
             failed.append(src)
     if failed:
         raise RuntimeError(f"hipcc failed for {failed}")
-    tmp = LIB_PATH + ".tmp"
+    tmp = lib_path + ".tmp"
     cmd = [cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, lib_path)
+    return lib_path
 
 
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv[1:]))
+    print(build(verbose="-v" in sys.argv[1:], poison=True))

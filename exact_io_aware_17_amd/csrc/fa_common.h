@@ -98,20 +98,34 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(size_t)(__attribute__((address_space(3))) const void*)p;
 }
 
-// Direct global -> LDS copy of 16 bytes per lane: lane l's bytes land at LDS
-// byte `lds_base + 16 l` (lds_base must be wave-uniform). Issued through
+// Direct global -> LDS copies of 16 bytes per lane: lane l's bytes land at
+// LDS byte `lds_base + 16 l` (lds_base must be wave-uniform). Issued through
 // inline assembly so that the compiler does not make every later LDS read
 // wait for these copies; callers wait with wait_vmcnt0() before the barrier
 // that publishes the data.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds_base) : "memory", "m0");
+
+// Debug builds with FA_LDS_POISON: before a copy is issued, the 16 bytes it
+// will write are set to all-ones (NaN in bf16, fp32 and E4M3). A reader that
+// runs ahead of the copy's wait and barrier, or lags behind the next copy into
+// the same slot, then reads NaN, which reaches O and fails every parity test,
+// instead of reading finite stale data.
+__device__ __forceinline__ void lds_poison16(uint32_t lds_base) {
+#ifdef FA_LDS_POISON
+  typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+  lds_u32x4* p = (lds_u32x4*)(size_t)(lds_base + 16u * (threadIdx.x & 63u));
+  *p = u32x4{0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu};
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#else
+  (void)lds_base;
+#endif
 }
 
 // Same copy with a wave-uniform 64-bit global base in SGPRs and a 32-bit
 // per-lane byte offset (no per-lane 64-bit address arithmetic).
 __device__ __forceinline__ void dma16_sbase(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  lds_poison16(lds_base);
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds_base)
                : "memory", "m0");
 }

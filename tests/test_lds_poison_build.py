@@ -1,0 +1,46 @@
+"""The LDS-poisoning debug build (host only): compiled with FA_LDS_POISON, the
+forward kernels store all-ones to each copy's LDS destination right before the
+copy is issued; the regular build has no such stores."""
+import os
+import re
+import subprocess
+
+import pytest
+
+from exact_io_aware_17_amd import build as B
+
+
+def _asm(extra):
+    src = os.path.join(B.CSRC, "fa_fwd.hip")
+    r = subprocess.run([B.hipcc(), *B.HIP_FLAGS, *extra, "--cuda-device-only", "-S", src, "-o", "-"],
+                       capture_output=True, text=True)
+    if r.returncode:
+        pytest.skip(f"hipcc could not compile: {r.stderr[:200]}")
+    return r.stdout
+
+
+def _poisoned_copies(asm):
+    """Copies whose preceding instructions (after the previous copy) store
+    16 bytes to LDS and wait for it."""
+    lines = [ln.strip() for ln in asm.splitlines() if ln.strip() and not ln.strip().startswith(";")]
+    n_copy, n_poisoned, since = 0, 0, []
+    for ln in lines:
+        if ln.startswith("global_load_lds_dwordx4"):
+            n_copy += 1
+            window = since[-8:]
+            if any(x.startswith("ds_write_b128") for x in window) and any("lgkmcnt(0)" in x for x in window):
+                n_poisoned += 1
+            since = []
+        else:
+            since.append(ln)
+    return n_copy, n_poisoned
+
+
+def test_poison_build_stores_before_every_copy():
+    n, p = _poisoned_copies(_asm(["-DFA_LDS_POISON"]))
+    assert n > 0 and p == n, (n, p)
+
+
+def test_regular_build_has_no_poison_stores():
+    n, p = _poisoned_copies(_asm([]))
+    assert n > 0 and p == 0, (n, p)
