@@ -9,7 +9,8 @@ when their source hash matches) and a bounded CPU-oracle baseline:
     with and without the causal mask, long causal B1 H32 16384^2);
   - the split-KV decode workload (B=64, Hq=32, Hkv=8, Nk=8192, 16 splits) and
     the same decode over a paged K/V cache (16-key pages in a random order);
-  - the pages' shape with OCP E4M3 inputs (fa_fwd_fp8) and at head size 256;
+  - the pages' shape with OCP E4M3 inputs (fa_fwd_fp8) and at head sizes 256
+    and 192;
   - the backward pass (fa_bwd) on the pages' shape;
 and the machine: ROCm version and the shader clock rocm-smi reports while the
 pages' shape runs back to back.
@@ -43,6 +44,7 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
 PREFILL = "pages_shape_h8_q4096_kv8192"
 PREFILL_FP8 = "pages_shape_fp8_h8_q4096_kv8192"
 PREFILL_D256 = "pages_shape_d256_h8_q4096_kv8192"
+PREFILL_D192 = "pages_shape_d192_h8_q4096_kv8192"
 DECODE = "gqa_decode_b64_hq32_hkv8_kv8192"
 # The other prefill workloads, each timed in the default line with its own
 # roofline and CPU baseline (the first is launch-bound: 8 workgroups).
@@ -66,7 +68,7 @@ def kernel_source_sha(files):
 
 FWD_SOURCES = ["fa_fwd.hip", "fa_common.h"]
 FWD8_SOURCES = ["fa_fwd_fp8.hip", "fa_common.h"]
-FWD256_SOURCES = ["fa_fwd_d256.hip", "fa_common.h"]
+FWD256_SOURCES = ["fa_fwd_wide.hip", "fa_common.h"]
 BWD_SOURCES = ["fa_bwd.hip", "fa_common.h"]
 DEC_SOURCES = ["fa_splitkv.hip", "fa_common.h"]
 
@@ -397,7 +399,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--all", action="store_true", help="(kept for old command lines; the other prefill "
                                                           "workloads are always timed)")
-    ap.add_argument("--only", choices=["prefill", "prefill_fp8", "prefill_d256", "backward", "decode", "decode_paged"],
+    ap.add_argument("--only", choices=["prefill", "prefill_fp8", "prefill_d256", "prefill_d192", "backward", "decode",
+                                       "decode_paged"],
                     default=None)
     ap.add_argument("--workload", default=None, help="with --only prefill: the prefill workload (synth name)")
     ap.add_argument("--copy-calib", action="store_true")
@@ -429,9 +432,10 @@ def main():
         r = bench_backward(wp, args.steps, args.warmup, device, min_warm_s=0.0)
         print(json.dumps({"only": "backward", **r}))
         return
-    if args.only == "prefill_d256":
-        r = bench_prefill(synth.WORKLOADS[PREFILL_D256], args.steps, args.warmup, device, min_warm_s=0.0)
-        print(json.dumps({"only": "prefill_d256", **r}))
+    if args.only in ("prefill_d256", "prefill_d192"):
+        name = PREFILL_D256 if args.only == "prefill_d256" else PREFILL_D192
+        r = bench_prefill(synth.WORKLOADS[name], args.steps, args.warmup, device, min_warm_s=0.0)
+        print(json.dumps({"only": args.only, **r}))
         return
     if args.only == "prefill_fp8":
         r = bench_prefill_fp8(synth.WORKLOADS[PREFILL_FP8], args.steps, args.warmup, device, min_warm_s=0.0)
@@ -457,6 +461,10 @@ def main():
     log(f"prefill d256 {w256.name}: warmup {args.warmup}, steps {args.steps}")
     r256 = bench_prefill(w256, args.steps, args.warmup, device)
     log(f"  {r256}")
+    w192 = synth.WORKLOADS[PREFILL_D192]
+    log(f"prefill d192 {w192.name}: warmup {args.warmup}, steps {args.steps}")
+    r192 = bench_prefill(w192, args.steps, args.warmup, device)
+    log(f"  {r192}")
     bsteps, bwarm = max(1, args.steps // 5), max(1, args.warmup // 5)
     log(f"backward {wp.name}: warmup {bwarm}, steps {bsteps}")
     rb = bench_backward(wp, bsteps, bwarm, device)
@@ -531,7 +539,18 @@ def main():
                                       "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                                       "frac": round(r256["kernel_tflops"] / PEAK_BF16_TFLOPS, 4),
                                       "traffic": fwd256_traffic, "kernel_ms": round(r256["kernel_ms"], 5),
-                                      "kernel": "fwd_bf16_d256_kernel<2>"}},
+                                      "kernel": "fwd_bf16_wide_kernel<256, 2>"}},
+        "prefill_d192": {"workload": w192.name, "dtype": "bf16", "d": 192,
+                         "metric": "attention fwd TFLOPS (4*B*H*Nq*Nk*d per forward)",
+                         "value": round(r192["tflops"], 2), "unit": "TFLOP/s",
+                         "ms_per_step": round(r192["ms_per_step"], 5),
+                         "roofline": {"bound": "mfma", "achieved": round(r192["kernel_tflops"], 2),
+                                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                                      "frac": round(r192["kernel_tflops"] / PEAK_BF16_TFLOPS, 4),
+                                      "traffic": traffic_from_profile("fwd_bf16_d192_pages_shape_traffic.md",
+                                                                      FWD256_SOURCES),
+                                      "kernel_ms": round(r192["kernel_ms"], 5),
+                                      "kernel": "fwd_bf16_wide_kernel<192, 2>"}},
         "backward": {"workload": wp.name, "dtype": "bf16",
                      "metric": "attention bwd TFLOPS (2.5 x 4*B*H*Nq*Nk*d: the five products)",
                      "value": round(rb["tflops"], 2), "unit": "TFLOP/s", "steps": bsteps, "warmup": bwarm,

@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(HERE, "libfa.so")
 # (FA_LDS_POISON), so that a read racing a copy shows up as NaN in O.
 POISON_BUILD_DIR = os.path.join(HERE, "_build_poison")
 POISON_LIB_PATH = os.path.join(HERE, "libfa_poison.so")
-SOURCES = ["fa_api.hip", "fa_fwd.hip", "fa_fwd_d256.hip", "fa_fwd_fp8.hip", "fa_fp32.hip", "fa_splitkv.hip", "fa_bwd.hip"]
+SOURCES = ["fa_api.hip", "fa_fwd.hip", "fa_fwd_wide.hip", "fa_fwd_fp8.hip", "fa_fp32.hip", "fa_splitkv.hip", "fa_bwd.hip"]
 ARCH = "gfx950"
 
 # Packed-fp32 VALU forms are kept out of the generated code.

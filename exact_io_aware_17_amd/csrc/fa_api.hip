@@ -44,7 +44,7 @@ fa_status check_common(const void* q, const void* k, const void* v, const void* 
   const long long nq = elems4(B, Hq, Nq, d), nkv = elems4(B, Hkv, Nk, d);
   if (nq < 0 || nkv < 0) return FA_ERR_SHAPE;
   if ((long long)B * Hq > 0x7fffffffLL || (long long)B * Hkv > 0x7fffffffLL) return FA_ERR_SHAPE;
-  if (d != 64 && d != 128 && d != 256) return FA_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128 && d != 192 && d != 256) return FA_ERR_UNSUPPORTED;
   if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_ARG;
   if (causal != 0 && causal != 1) return FA_ERR_ARG;
   // Pointers of empty tensors may be NULL (allocators hand out NULL for them).
@@ -147,14 +147,14 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
   if (st != FA_OK) return st;
   if (fa::fwd_bf16_grid(B, Hq, Nq) > kMaxGridX) return FA_ERR_UNSUPPORTED;
   fa::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal, stream};
-  return launched(d == 256 ? fa::launch_fwd_bf16_d256(a) : fa::launch_fwd_bf16(a));
+  return launched(d > 128 ? fa::launch_fwd_bf16_wide(a) : fa::launch_fwd_bf16(a));
 }
 
 fa_status fa_fwd_fp32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int Hq,
                       int Hkv, int Nq, int Nk, int d, float scale, int causal, void* stream) {
   fa_status st = check_common(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal);
   if (st != FA_OK) return st;
-  if (d == 256) return FA_ERR_UNSUPPORTED;
+  if (d > 128) return FA_ERR_UNSUPPORTED;
   if (fa::fwd_fp32_grid(B, Hq, Nq) > kMaxGridX) return FA_ERR_UNSUPPORTED;
   fa::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal, stream};
   return launched(fa::launch_fwd_fp32(a));
@@ -188,7 +188,7 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
                  int causal, void* workspace, size_t workspace_bytes, void* stream) {
   fa_status st = check_common(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal);
   if (st != FA_OK) return st;
-  if (d == 256) return FA_ERR_UNSUPPORTED;
+  if (d > 128) return FA_ERR_UNSUPPORTED;
   const long long nq = elems4(B, Hq, Nq, d), nkv = elems4(B, Hkv, Nk, d);
   if (nq > 0 && (!dout || !dq)) return FA_ERR_NULL;
   if (nkv > 0 && (!dk || !dv)) return FA_ERR_NULL;
@@ -221,7 +221,7 @@ fa_status fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, f
                          void* workspace, size_t workspace_bytes, void* stream) {
   fa_status st = check_common(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal);
   if (st != FA_OK) return st;
-  if (d == 256) return FA_ERR_UNSUPPORTED;
+  if (d > 128) return FA_ERR_UNSUPPORTED;
   if (num_splits < 1 || num_splits > kMaxSplits) return FA_ERR_ARG;
   size_t ob = 0, total = 0;
   if (!split_ws_sizes(B, Hq, Nq, d, num_splits, &ob, &total)) return FA_ERR_SHAPE;
@@ -249,7 +249,7 @@ fa_status fa_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, vo
                                  void* stream) {
   fa_status st = check_common(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal);
   if (st != FA_OK) return st;
-  if (d == 256) return FA_ERR_UNSUPPORTED;
+  if (d > 128) return FA_ERR_UNSUPPORTED;
   if (num_splits < 1 || num_splits > kMaxSplits) return FA_ERR_ARG;
   size_t ob = 0, total = 0;
   if (!split_ws_sizes(B, Hq, Nq, d, num_splits, &ob, &total)) return FA_ERR_SHAPE;
@@ -284,7 +284,7 @@ fa_status fa_fwd_splitkv_paged(const void* q, const void* k_cache, const void* v
   // The caches as [num_pages, Hkv, page_size, d] for the shared checks.
   fa_status st = check_common(q, k_cache, v_cache, o, lse, B, Hq, Hkv, Nq, 0, d, scale, causal);
   if (st != FA_OK) return st;
-  if (d == 256) return FA_ERR_UNSUPPORTED;
+  if (d > 128) return FA_ERR_UNSUPPORTED;
   if (elems4(num_pages, Hkv, page_size, d) < 0 || elems4(B, max_pages, 1, 1) < 0) return FA_ERR_SHAPE;
   if (num_splits < 1 || num_splits > kMaxSplits) return FA_ERR_ARG;
   size_t ob = 0, total = 0;

@@ -1,4 +1,4 @@
-// bf16 attention forward (prefill) for head size 256 on gfx950.
+// bf16 attention forward (prefill) for head sizes 192 and 256 on gfx950.
 //
 // Same algorithm as fa_fwd.hip (the FA2 loop of "Flash Attention on the 5090
 // in CUDA C++", "Flash Attention 2 algorithm" pseudocode, with the online
@@ -7,30 +7,35 @@
 // next" item: the page's note that head_dim 128 fits in registers no longer
 // holds, so the work split changes.
 //
-// Mapping to CDNA4 for d = 256:
+// Mapping to CDNA4 for d = 192, 256:
 //  * A workgroup owns 128 query rows, 32 per wave. Q stays in registers as
-//    the B operand of S^T = K Q^T (64 VGPRs), O^T is accumulated in 128
+//    the B operand of S^T = K Q^T (d / 4 VGPRs), O^T is accumulated in d / 2
 //    VGPRs, so a wave has at most 256 registers and a SIMD runs two waves,
 //    whose MFMA and VALU work overlap without a fixed phase order. The two
 //    waves come from one of two layouts (template NG):
 //    - NG = 2: 8 waves; waves 0-3 (group 0) and 4-7 (group 1) hold the same
 //      rows and take the even and the odd 32-key tiles, merged through LDS at
-//      the end; 130 KiB of LDS, one workgroup per CU. Used when the grid has
-//      fewer than two workgroups per CU (the pages' shape: 256).
-//    - NG = 1: 4 waves walking every tile; 64 KiB of LDS, two workgroups per
-//      CU, which also hide each other's prologue and epilogue. Used for
-//      grids of at least 512 workgroups (measured: 1047 vs 925 TFLOP/s at
-//      B4 H16 2048^2 d256, while NG = 2 gives 1058 vs 757 at the pages'
-//      shape with d = 256).
-//  * Each group double-buffers its own K and V tiles (16 KiB each). Per
-//    tile: scores in 16 MFMAs (32x32x16 bf16), the online softmax on 16
-//    scores per lane, P.V in 16 MFMAs; the group's next tile is copied
+//      the end; one workgroup per CU. Used when the grid has fewer than two
+//      workgroups per CU (the pages' shape: 256).
+//    - NG = 1: 4 waves walking every tile; two workgroups per CU, which also
+//      hide each other's prologue and epilogue. Used for grids of at least
+//      512 workgroups (measured at d = 256: 1047 vs 925 TFLOP/s at B4 H16
+//      2048^2, while NG = 2 gives 1058 vs 757 at the pages' shape).
+//  * Each group double-buffers its own K and V tiles (32 rows x 2 d bytes).
+//    Per tile: scores in d / 16 MFMAs (32x32x16 bf16), the online softmax on
+//    16 scores per lane, P.V in d / 16 MFMAs; the group's next tile is copied
 //    meanwhile (global -> LDS), one workgroup barrier per step.
 //  * Operand layouts are those of the d = 128 kernel: kappa() row order of
 //    the K operand puts P straight into the B-operand layout of O^T += V^T P^T;
-//    V^T comes from transposing LDS reads; the 16-byte chunks of a row are
-//    XORed with a bijection of the row's low 4 bits (512-byte rows start on
-//    bank 0, so only the chunk's low 4 bits pick banks).
+//    V^T comes from transposing LDS reads. The 16-byte chunks of a row are
+//    XOR-swizzled so that both the K reads (16 rows at one chunk per pass) and
+//    the transposing V reads (4 rows x 4 chunks per pass) hit distinct banks:
+//    512-byte rows (d = 256) start on bank 0 and take a bijection of the row's
+//    low 4 bits on chunk bits 0..3; 384-byte rows (d = 192, 24 chunks) start
+//    on bank 0 or 32 (by row parity) and take, within each group of 8
+//    chunks, an XOR with a row function that is a bijection over the 8 even
+//    and over the 8 odd rows of a 16-row block whose bit 2 differs between
+//    rows r and r + 2 of a 4-row group.
 #include "fa_common.h"
 #include "fa_internal.h"
 
@@ -40,56 +45,81 @@ namespace {
 constexpr int k2WavesPerGroup = 4;
 constexpr int k2BM = 128;
 constexpr int k2BN = 32;
-constexpr int k2D = 256;
-constexpr int k2RowB = k2D * 2;              // 512 bytes per row
-constexpr int k2Tile = k2BN * k2RowB;        // 16 KiB
-template <int NG>
-struct D256Layout {
+template <int D, int NG>
+struct WideLayout {
+  static constexpr int kRowB = D * 2;                        // bytes per row
+  static constexpr int kTile = k2BN * kRowB;                 // 12 or 16 KiB
+  static constexpr int kCopies = kTile / 1024 / k2WavesPerGroup;  // copy instructions per wave per tile
   static constexpr int kThreads = 64 * k2WavesPerGroup * NG;
-  static constexpr int kVBase = 2 * NG * k2Tile;  // two K slots per group, then two V slots per group
-  static constexpr int kMergeBytes = NG == 2 ? 4 * 8 * 16 * 64 * 4 + 2048 : 0;
+  static constexpr int kVBase = 2 * NG * kTile;  // two K slots per group, then two V slots per group
+  static constexpr int kMergeBytes = NG == 2 ? 4 * (D / 32) * 16 * 64 * 4 + 2048 : 0;
   static constexpr int kLds = kMergeBytes > 2 * kVBase ? kMergeBytes : 2 * kVBase + (NG == 2 ? 2048 : 0);
+  // Lane offsets kept per wave: at d = 256 copy instructions i and i + 2
+  // cover rows 16 apart with the same swizzle, so two offsets serve all four
+  // (the other two through a scalar base 16 rows further on).
+  static constexpr int kGoff = D == 256 ? 2 : kCopies;
+  static_assert(kTile % (1024 * k2WavesPerGroup) == 0, "tile must split evenly over the group's waves");
 };
-constexpr int k2Copies = k2Tile / 1024 / 4;  // 1 KiB copy instructions per wave per tile (4)
 constexpr float k2SumHi = 18446744073709551616.0f;  // 2^64, as in the d = 128 kernel
 
-__device__ __forceinline__ int swz256(int row, int chunk) {
-  return chunk ^ (((row & 3) << 2) | ((row >> 2) & 3));
+// Stored chunk of logical chunk c in row `row` (an involution for fixed row).
+template <int D>
+__device__ __forceinline__ int swz_wide(int row, int c) {
+  if constexpr (D == 256) {
+    return c ^ (((row & 3) << 2) | ((row >> 2) & 3));
+  } else {
+    const int f = ((row >> 2) & 3) | (((row >> 1) & 1) << 2);
+    return c ^ f;  // f < 8: stays within c's group of 8 chunks
+  }
 }
 
-// Copy one tile (32 rows x 512 bytes): instruction blk covers rows 2 blk,
-// 2 blk + 1 (lane l: row 2 blk + l / 32, LDS chunk l % 32). Rows at or past
-// nvalid fetch row nvalid - 1 (finite data, masked later). Wave w issues
-// blk = w + 4 i; instructions i and i + 2 cover rows 16 apart with the same
-// swizzle, so two lane offsets serve all four (the other two through a
-// scalar base 16 rows further on).
-__device__ __forceinline__ void tile256_to_lds(uint32_t slot_lds, const uint16_t* src, int nvalid,
-                                               const uint32_t (&goff)[2], int wave, int lane) {
+// Copy one tile (32 rows x 2 d bytes): copy instruction blk writes LDS chunks
+// 64 blk .. 64 blk + 63 of the tile (lane l: chunk 64 blk + l, i.e. row
+// (64 blk + l) / (d / 8), stored chunk the remainder), fetched from the
+// logical chunk whose swizzled position that is. Wave w issues blk = w + 4 i.
+// Rows at or past nvalid fetch row nvalid - 1 (finite data, masked later).
+template <int D>
+__device__ __forceinline__ void tile_wide_to_lds(uint32_t slot_lds, const uint16_t* src, int nvalid,
+                                                 const uint32_t (&goff)[WideLayout<D, 1>::kGoff], int wave,
+                                                 int lane) {
+  constexpr int CH = D / 8;
+  constexpr int NC = WideLayout<D, 1>::kCopies;
   if (nvalid >= k2BN) {
 #pragma unroll
-    for (int i = 0; i < k2Copies; ++i)
-      dma16_sbase(src + (i >> 1) * 16 * k2D, goff[i & 1], slot_lds + (wave + 4 * i) * 1024);
+    for (int i = 0; i < NC; ++i) {
+      if constexpr (D == 256) {
+        dma16_sbase(src + (i >> 1) * 16 * D, goff[i & 1], slot_lds + (wave + 4 * i) * 1024);
+      } else {
+        dma16_sbase(src, goff[i], slot_lds + (wave + 4 * i) * 1024);
+      }
+    }
   } else {
 #pragma unroll
-    for (int i = 0; i < k2Copies; ++i) {
+    for (int i = 0; i < NC; ++i) {
       const int blk = wave + 4 * i;
-      const int row = blk * 2 + (lane >> 5);
+      const int flat = blk * 64 + lane;
+      const int row = flat / CH, ch = flat - row * CH;
       const int srow = row < nvalid ? row : nvalid - 1;
-      dma16_sbase(src, (uint32_t)(srow * k2RowB + swz256(row, lane & 31) * 16), slot_lds + blk * 1024);
+      dma16_sbase(src, (uint32_t)(srow * D * 2 + swz_wide<D>(row, ch) * 16), slot_lds + blk * 1024);
     }
   }
 }
 
-template <int NG>
-__global__ __launch_bounds__(64 * k2WavesPerGroup * NG, 2 / NG) void fwd_bf16_d256_kernel(
+template <int D, int NG>
+__global__ __launch_bounds__(64 * k2WavesPerGroup * NG, 2 / NG) void fwd_bf16_wide_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int Hq, int Hkv, int Nq, int Nk, float sl2, int causal,
     int n_qt, int n_wg) {
-  constexpr int D = k2D, BN = k2BN;
-  constexpr int k2VBase = D256Layout<NG>::kVBase;
-  // 64 KiB of tiles per group; with two groups the merge then reuses them
+  using L = WideLayout<D, NG>;
+  constexpr int BN = k2BN;
+  constexpr int KS = D / 16;  // k-steps of the score product
+  constexpr int DB = D / 32;  // 32-row blocks of O^T
+  constexpr int k2RowB = L::kRowB;
+  constexpr int k2Tile = L::kTile;
+  constexpr int k2VBase = L::kVBase;
+  // Four tile slots per group; with two groups the merge then reuses them
   // and the 2 KiB after them.
-  __shared__ __attribute__((aligned(1024))) uint16_t lds[D256Layout<NG>::kLds / sizeof(uint16_t)];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[L::kLds / sizeof(uint16_t)];
   const char* lds_c = reinterpret_cast<const char*>(lds);
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -113,16 +143,16 @@ __global__ __launch_bounds__(64 * k2WavesPerGroup * NG, 2 / NG) void fwd_bf16_d2
   const int diag = Nk - Nq;
 
   // Q rows as B operands: k-step s covers d = 16 s .. 16 s + 15.
-  bf16x8 qf[16];
+  bf16x8 qf[KS];
 #pragma unroll
-  for (int s = 0; s < 16; ++s)
+  for (int s = 0; s < KS; ++s)
     qf[s] = qrow < Nq ? *reinterpret_cast<const bf16x8*>(Qh + (size_t)qrow * D + s * 16 + hl * 8) : bf16x8{};
 
   // K operand of k-step s: row kappa(lane % 32), chunk 2 s + hl, i.e. byte
   // krow + ((2 s) ^ kx) * 16 with kx = hl ^ (the row's swizzle); computed per
   // read (two VALU) to keep registers for Q and O.
   const uint32_t krow = kappa(lane & 31) * k2RowB + 2 * grp * k2Tile;  // + the group's slots
-  const uint32_t kx = (uint32_t)swz256(kappa(lane & 31), hl);
+  const uint32_t kx = (uint32_t)swz_wide<D>(kappa(lane & 31), hl);
   // V^T operand (two transposing reads r = 0, 1 per MFMA): lane reads row
   // hl*8 + e + 4 r, chunk 4 db + 2 q16 + j/2, byte half j % 2, i.e. byte
   // vrow[r] + ((4 db) ^ vx[r]) * 16 with vx[r] = (2 q16 + j/2) ^ (the row's
@@ -134,14 +164,15 @@ __global__ __launch_bounds__(64 * k2WavesPerGroup * NG, 2 / NG) void fwd_bf16_d2
     for (int r = 0; r < 2; ++r) {
       const int row = hl * 8 + e + 4 * r;
       vrow[r] = k2VBase + 2 * grp * k2Tile + row * k2RowB + (j & 1) * 8;
-      vx[r] = (uint32_t)swz256(row, q16 * 2 + (j >> 1));
+      vx[r] = (uint32_t)swz_wide<D>(row, q16 * 2 + (j >> 1));
     }
   }
-  uint32_t goff[2];
+  uint32_t goff[L::kGoff];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int row = (rw + 4 * i) * 2 + (lane >> 5);
-    goff[i] = (uint32_t)(row * k2RowB + swz256(row, lane & 31) * 16);
+  for (int i = 0; i < L::kGoff; ++i) {
+    const int flat = (rw + 4 * i) * 64 + lane;
+    const int row = flat / (D / 8), ch = flat - row * (D / 8);
+    goff[i] = (uint32_t)(row * k2RowB + swz_wide<D>(row, ch) * 16);
   }
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(lds));
 
@@ -158,16 +189,16 @@ __global__ __launch_bounds__(64 * k2WavesPerGroup * NG, 2 / NG) void fwd_bf16_d2
     n_vis = nv < n_tiles ? (int)nv : n_tiles;
   }
 
-  f32x16 o[8];
+  f32x16 o[DB];
 #pragma unroll
-  for (int db = 0; db < 8; ++db) o[db] = f32x16{};
+  for (int db = 0; db < DB; ++db) o[db] = f32x16{};
   float m_run = 0.f, l_run = 0.f;
 
   // Group g takes tiles g, g + NG, g + 2 NG, ...; its u-th tile
   // (t = NG u + g) lives in slot 2 g + u % 2 of the K and of the V slots.
   auto load = [&](int t, int slot) __attribute__((always_inline)) {
-    tile256_to_lds(lds0 + slot * k2Tile, Kh + (size_t)t * BN * D, Nk - t * BN, goff, rw, lane);
-    tile256_to_lds(lds0 + k2VBase + slot * k2Tile, Vh + (size_t)t * BN * D, Nk - t * BN, goff, rw, lane);
+    tile_wide_to_lds<D>(lds0 + slot * k2Tile, Kh + (size_t)t * BN * D, Nk - t * BN, goff, rw, lane);
+    tile_wide_to_lds<D>(lds0 + k2VBase + slot * k2Tile, Vh + (size_t)t * BN * D, Nk - t * BN, goff, rw, lane);
   };
 
   // One tile from the group's K/V slot PAR (the group's base is in krow and
@@ -176,14 +207,14 @@ __global__ __launch_bounds__(64 * k2WavesPerGroup * NG, 2 / NG) void fwd_bf16_d2
     constexpr uint32_t KB = decltype(par_c)::value * k2Tile;
     f32x16 sc = f32x16{};
 #pragma unroll
-    for (int s = 0; s < 16; ++s) {
+    for (int s = 0; s < KS; ++s) {
       const bf16x8 a = *reinterpret_cast<const bf16x8*>(lds_c + krow + (((uint32_t)(2 * s) ^ kx) << 4) + KB);
       sc = mfma32(a, qf[s], sc);
     }
     // K-operand reads four ahead of their MFMAs (bounded register use).
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-    for (int s = 0; s < 12; ++s) {
+    for (int s = 0; s < KS - 4; ++s) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
@@ -221,7 +252,7 @@ __global__ __launch_bounds__(64 * k2WavesPerGroup * NG, 2 / NG) void fwd_bf16_d2
       const float alpha = l_run == 0.f ? 1.f : fast_exp2(m_run - m_new);
       l_run *= alpha;
 #pragma unroll
-      for (int db = 0; db < 8; ++db) o[db] *= alpha;
+      for (int db = 0; db < DB; ++db) o[db] *= alpha;
       m_run = m_new;
       tot = exps();
     }
@@ -229,7 +260,7 @@ __global__ __launch_bounds__(64 * k2WavesPerGroup * NG, 2 / NG) void fwd_bf16_d2
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-      for (int db = 0; db < 8; ++db) {
+      for (int db = 0; db < DB; ++db) {
         const uint32_t base = KB + hf * 16 * k2RowB;
         const uint32_t a0 = vrow[0] + (((uint32_t)(4 * db) ^ vx[0]) << 4) + base;
         const uint32_t a1 = vrow[1] + (((uint32_t)(4 * db) ^ vx[1]) << 4) + base;
@@ -240,7 +271,7 @@ __global__ __launch_bounds__(64 * k2WavesPerGroup * NG, 2 / NG) void fwd_bf16_d2
     // V^T reads four MFMAs ahead.
     __builtin_amdgcn_sched_group_barrier(0x100, 8, 1);
 #pragma unroll
-    for (int s = 0; s < 12; ++s) {
+    for (int s = 0; s < 2 * DB - 4; ++s) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
     }
@@ -250,7 +281,7 @@ __global__ __launch_bounds__(64 * k2WavesPerGroup * NG, 2 / NG) void fwd_bf16_d2
   if (grp < n_tiles) load(grp, 2 * grp);
   wait_vmcnt0();
 #pragma unroll
-  for (int s = 0; s < 16; ++s) asm volatile("" ::"v"(qf[s]));
+  for (int s = 0; s < KS; ++s) asm volatile("" ::"v"(qf[s]));
   __syncthreads();
   // Step u: group g computes its tile t = NG u + g from slot 2 g + u % 2
   // while its next tile (t + NG) is copied into slot 2 g + (u + 1) % 2. That
@@ -273,14 +304,14 @@ __global__ __launch_bounds__(64 * k2WavesPerGroup * NG, 2 / NG) void fwd_bf16_d2
   }
 
   // Merge the two groups (same rows, disjoint key sets) and write out.
-  float* xo = reinterpret_cast<float*>(lds);                       // [4 rw][8 db][16][64] fp32 = 128 KiB
-  float* xm = reinterpret_cast<float*>(lds) + 4 * 8 * 16 * 64;     // [4 rw][64] m, then [4 rw][64] l
+  float* xo = reinterpret_cast<float*>(lds);                        // [4 rw][DB][16][64] fp32
+  float* xm = reinterpret_cast<float*>(lds) + 4 * DB * 16 * 64;     // [4 rw][64] m, then [4 rw][64] l
   if (NG == 1) {
     if (qrow < Nq) {
       const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
       uint16_t* orow = O + ((size_t)bh * Nq + qrow) * D;
 #pragma unroll
-      for (int db = 0; db < 8; ++db)
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
           const int d = db * 32 + i4 * 8 + hl * 4;
@@ -295,9 +326,9 @@ __global__ __launch_bounds__(64 * k2WavesPerGroup * NG, 2 / NG) void fwd_bf16_d2
   }
   if (grp == 1) {
 #pragma unroll
-    for (int db = 0; db < 8; ++db)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) xo[((rw * 8 + db) * 16 + i) * 64 + lane] = o[db][i];
+      for (int i = 0; i < 16; ++i) xo[((rw * DB + db) * 16 + i) * 64 + lane] = o[db][i];
     xm[rw * 64 + lane] = m_run;
     xm[256 + rw * 64 + lane] = l_run;
   }
@@ -313,7 +344,7 @@ __global__ __launch_bounds__(64 * k2WavesPerGroup * NG, 2 / NG) void fwd_bf16_d2
     const float c0 = a0 * inv, c1 = a1 * inv;
     uint16_t* orow = O + ((size_t)bh * Nq + qrow) * D;
 #pragma unroll
-    for (int db = 0; db < 8; ++db)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
         const int d = db * 32 + i4 * 8 + hl * 4;
@@ -321,7 +352,7 @@ __global__ __launch_bounds__(64 * k2WavesPerGroup * NG, 2 / NG) void fwd_bf16_d2
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int i = i4 * 4 + j;
-          v[j] = o[db][i] * c0 + xo[((rw * 8 + db) * 16 + i) * 64 + lane] * c1;
+          v[j] = o[db][i] * c0 + xo[((rw * DB + db) * 16 + i) * 64 + lane] * c1;
         }
         u32x2 w;
         w[0] = pack_bf16x2(v[0], v[1]);
@@ -332,27 +363,32 @@ __global__ __launch_bounds__(64 * k2WavesPerGroup * NG, 2 / NG) void fwd_bf16_d2
   }
 }
 
-}  // namespace
-
 // Grids of at least this many workgroups use the one-group layout (two
 // workgroups per CU on the 256 CUs).
-constexpr long kD256OneGroupMinWg = 512;
+constexpr long kWideOneGroupMinWg = 512;
 
-hipError_t launch_fwd_bf16_d256(const FwdArgs& a) {
+template <int D>
+hipError_t launch_wide_d(const FwdArgs& a) {
   const int n_qt = (a.Nq + k2BM - 1) / k2BM;
   const long n_wg = (long)a.B * a.Hq * n_qt;
   if (n_wg == 0) return hipSuccess;
   const float sl2 = a.scale * kLog2e;
-  if (n_wg >= kD256OneGroupMinWg) {
-    hipLaunchKernelGGL(fwd_bf16_d256_kernel<1>, dim3((unsigned)n_wg), dim3(D256Layout<1>::kThreads), 0,
+  if (n_wg >= kWideOneGroupMinWg) {
+    hipLaunchKernelGGL((fwd_bf16_wide_kernel<D, 1>), dim3((unsigned)n_wg), dim3(WideLayout<D, 1>::kThreads), 0,
                        (hipStream_t)a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                        (uint16_t*)a.o, a.lse, a.Hq, a.Hkv, a.Nq, a.Nk, sl2, a.causal, n_qt, (int)n_wg);
   } else {
-    hipLaunchKernelGGL(fwd_bf16_d256_kernel<2>, dim3((unsigned)n_wg), dim3(D256Layout<2>::kThreads), 0,
+    hipLaunchKernelGGL((fwd_bf16_wide_kernel<D, 2>), dim3((unsigned)n_wg), dim3(WideLayout<D, 2>::kThreads), 0,
                        (hipStream_t)a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                        (uint16_t*)a.o, a.lse, a.Hq, a.Hkv, a.Nq, a.Nk, sl2, a.causal, n_qt, (int)n_wg);
   }
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd_bf16_wide(const FwdArgs& a) {
+  return a.d == 256 ? launch_wide_d<256>(a) : launch_wide_d<192>(a);
 }
 
 }  // namespace fa

@@ -52,7 +52,7 @@ struct BwdArgs {
 };
 
 hipError_t launch_fwd_bf16(const FwdArgs& a);       // d = 64, 128
-hipError_t launch_fwd_bf16_d256(const FwdArgs& a);  // d = 256
+hipError_t launch_fwd_bf16_wide(const FwdArgs& a);  // d = 192, 256
 hipError_t launch_fwd_fp32(const FwdArgs& a);
 // q, k, v of `a` are E4M3 bytes (d = 128); o is bf16, lse fp32.
 hipError_t launch_fwd_fp8(const FwdArgs& a, float q_descale, float k_descale, float v_descale);

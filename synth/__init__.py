@@ -99,6 +99,9 @@ WORKLOADS = {
     "pages_shape_d256_h8_q4096_kv8192": Workload(
         "pages_shape_d256_h8_q4096_kv8192", 1, 8, 8, 4096, 8192, 256,
         note="the pages' shape at head size 256"),
+    "pages_shape_d192_h8_q4096_kv8192": Workload(
+        "pages_shape_d192_h8_q4096_kv8192", 1, 8, 8, 4096, 8192, 192,
+        note="the pages' shape at head size 192"),
     "pages_shape_fp8_h8_q4096_kv8192": Workload(
         "pages_shape_fp8_h8_q4096_kv8192", 1, 8, 8, 4096, 8192, 128,
         note="the pages' shape with OCP E4M3 inputs and per-tensor descale factors"),

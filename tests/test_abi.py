@@ -69,7 +69,9 @@ def test_forward_argument_checks(entry):
     assert f(d=96) == 3
     assert f(d=512) == 3
     if entry == "fa_fwd_fp32":
-        assert f(d=256) == 3  # head size 256: bf16 prefill only
+        assert f(d=256) == 3  # head sizes 192 and 256: bf16 prefill only
+        assert f(d=192) == 3
+    assert f(d=160) == 3
     for s in (0.0, -0.5, math.inf, math.nan):
         assert f(scale=s) == 7, s
     assert f(causal=2) == 7

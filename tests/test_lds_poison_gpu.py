@@ -45,6 +45,7 @@ CASES = [
     synth.Workload("poison_long_keys", 1, 2, 1, 130, 1500, 128, seed=9),
     synth.Workload("poison_d256_causal", 1, 2, 2, 384, 384, 256, causal=True),
     synth.Workload("poison_d256_ragged_gqa", 2, 4, 2, 200, 333, 256, seed=1),
+    synth.Workload("poison_d192_ragged_gqa_causal", 2, 4, 2, 200, 333, 192, causal=True, seed=12),
 ]
 
 

@@ -100,6 +100,16 @@ D256 = [
     # 8 x 64 heads x 2 query blocks = 1024 workgroups: the one-group layout.
     synth.Workload("d256_many_blocks_gqa_causal_ragged", 8, 64, 8, 130, 77, 256, causal=True, seed=7),
     synth.Workload("d256_many_blocks_ragged", 4, 64, 16, 200, 90, 256, seed=8),
+    # Head size 192 (384-byte rows, 24 chunks: a copy instruction covers 2 2/3
+    # rows, and the swizzle works within groups of 8 chunks).
+    synth.Workload("d192_single_head_n256", 1, 1, 1, 256, 256, 192),
+    synth.Workload("d192_ragged_gqa", 2, 4, 2, 200, 333, 192, seed=11),
+    synth.Workload("d192_ragged_gqa_causal", 2, 4, 2, 200, 333, 192, causal=True, seed=12),
+    synth.Workload("d192_more_queries_than_keys_causal", 1, 3, 1, 300, 70, 192, causal=True, seed=13),
+    synth.Workload("d192_one_query_one_key", 1, 1, 1, 1, 1, 192),
+    synth.Workload("d192_keys_below_one_tile", 1, 2, 2, 300, 17, 192, seed=14),
+    synth.Workload("d192_odd_tiles_causal", 1, 2, 1, 161, 161, 192, causal=True, seed=15),
+    synth.Workload("d192_many_blocks_gqa_causal_ragged", 8, 64, 8, 130, 77, 192, causal=True, seed=16),
 ]
 
 
@@ -113,11 +123,14 @@ def test_bf16_d256_full_oracle(w):
 
 
 @pytest.mark.parametrize("name", ["pages_shape_d256_h8_q4096_kv8192", "batched_d256_b4h16_n2048",
-                                  "batched_d256_b4h16_n2048_causal"])
+                                  "batched_d256_b4h16_n2048_causal", "pages_shape_d192_h8_q4096_kv8192",
+                                  "batched_d192_b4h16_n2048_causal"])
 def test_bf16_d256_full_size_sampled(name):
-    """Full-size d = 256 launches: the pages' shape (256 workgroups, the
-    two-group layout) and the batched shape (1024, the one-group layout)."""
-    w = W.get(name) or synth.Workload(name, 4, 16, 16, 2048, 2048, 256, causal=name.endswith("causal"))
+    """Full-size d = 256 and d = 192 launches: the pages' shape (256
+    workgroups, the two-group layout) and the batched shape (1024, the
+    one-group layout)."""
+    d = 192 if "d192" in name else 256
+    w = W.get(name) or synth.Workload(name, 4, 16, 16, 2048, 2048, d, causal=name.endswith("causal"))
     say(f"case bf16 d256 full-size {w.name}")
     o, lse = _run_fwd(w)
     rows = sample_rows(w.Nq)
