@@ -35,7 +35,7 @@
  *     clears) the calling thread's pending HIP error.
  *   - B, Nq, Nk may be 0 (nothing to compute, or every row without keys).
  *     Hq, Hkv >= 1 and Hq % Hkv == 0.  d must be 64 or 128 (fa_fwd also
- *     takes 256; the others return FA_ERR_UNSUPPORTED for it).
+ *     takes 192 and 256; the others return FA_ERR_UNSUPPORTED for them).
  *     scale must be finite and > 0.  causal must be 0 or 1.
  */
 #ifndef FA_H
@@ -64,8 +64,8 @@ typedef enum fa_status {
  * nearest even), lse [B,Hq,Nq] fp32 out.  Products run in bf16 with fp32
  * accumulation; the softmax runs in fp32; probabilities are rounded to bf16
  * before the P.V product while the row sums use the unrounded values.
- * d = 64, 128 or 256 (head size 256, the 5090 page's "What next" item, runs
- * on its own kernel: 4 waves per 128 query rows, 32-key tiles).
+ * d = 64, 128, 192 or 256 (head sizes above 128, the 5090 page's "What next"
+ * item, run on their own kernel: 4 waves per 128 query rows, 32-key tiles).
  * o and lse must not overlap the inputs.
  */
 fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
