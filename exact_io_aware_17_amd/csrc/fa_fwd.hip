@@ -9,10 +9,21 @@
 // unnormalised form with a single division at the end.
 //
 // Mapping to CDNA4 (our design; the page's sm120 kernel is prior art only):
-//  * 512 threads = 8 waves, two waves per SIMD. Waves 0-3 and 4-7 form two
-//    groups that own the same 128 query rows (32 rows per wave); group 0 takes
-//    the even KV tiles, group 1 the odd ones, and the two partial results are
-//    merged once at the end (same rescale, applied to the two halves).
+//  * 512 threads = 8 waves, two waves per SIMD, 32 query rows per wave. Waves
+//    0-3 and 4-7 form two groups in one of two layouts (template ROWG):
+//    - row groups (ROWG): the workgroup owns 256 rows, each group 128 of
+//      them, and both groups walk every KV tile, so each K/V tile copied into
+//      LDS feeds 256 rows. Used when the grid of 256-row blocks still fills
+//      the chip.
+//    - KV-parity groups: both groups own the same 128 rows; group 0 takes
+//      the even KV tiles, group 1 the odd ones, and the two partial results
+//      are merged once at the end (same rescale, applied to the two halves).
+//      Twice the row blocks, for grids that 256-row blocks would leave short
+//      of the 256 CUs.
+//    Each tile copy costs its issuing wave time that the softmax is not
+//    running, and the copies per MFMA are what the two layouts differ in: row
+//    groups copy one K and one V tile per step for 512 MFMAs per SIMD pair,
+//    KV-parity groups two of each.
 //  * Scores are computed transposed, S^T = K Q^T, with 32x32x16 bf16 MFMAs.
 //    The wave's Q rows are the B operand and stay in registers for the whole
 //    loop; every lane then holds the scores of ONE query row, so the row max
@@ -102,9 +113,9 @@ __device__ __forceinline__ void tile_to_lds(uint32_t slot_lds, const uint16_t* s
 
 // PAIRED (causal only): each workgroup takes query blocks n_qt - 1 - p and p of
 // one head, one after the other, so that every workgroup has the same number
-// of visible key tiles (2 (n_qt + 1) per pair) instead of 2 (qt + 1) for
-// block qt alone.
-template <int D, bool PAIRED>
+// of visible key tiles ((BM / 64) (n_qt + 1) per pair, instead of
+// (BM / 64) (qt + 1) for block qt alone).
+template <int D, bool PAIRED, bool ROWG>
 __global__ __launch_bounds__(kFwdThreads) void fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int Hq, int Hkv, int Nq, int Nk, float sl2, int causal,
@@ -133,7 +144,10 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_bf16_kernel(
   const uint16_t* Kh = K + (size_t)(b * Hkv + g) * Nk * D;
   const uint16_t* Vh = V + (size_t)(b * Hkv + g) * Nk * D;
 
-  const int qw0 = qt * kFwdBM + rw * 32;
+  constexpr int BM = ROWG ? 2 * kFwdBM : kFwdBM;
+  // Row groups: wave rw of group g holds 32-row block 2 rw + g (the two waves
+  // of a SIMD hold adjacent blocks); KV-parity groups: both hold block rw.
+  const int qw0 = qt * BM + (ROWG ? 2 * rw + grp : rw) * 32;
   const int qrow = qw0 + (lane & 31);
   const int diag = Nk - Nq;  // key j visible to row i iff j <= i + diag
 
@@ -173,7 +187,7 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_bf16_kernel(
 
   int kv_end = Nk;
   if (causal) {
-    const long last = (long)qt * kFwdBM + kFwdBM - 1 + diag;
+    const long last = (long)qt * BM + BM - 1 + diag;
     kv_end = last < 0 ? 0 : (int)(last + 1 < (long)Nk ? last + 1 : Nk);
   }
   const int n_tiles = (kv_end + BN - 1) / BN;
@@ -308,7 +322,11 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_bf16_kernel(
   // registers are consumed right after the common wait, so that the
   // compiler's own wait for them (which would also wait for every tile copy
   // in flight) is placed here and not inside the loop.
-  if (grp == 1) {
+  if constexpr (ROWG) {
+    if (n_tiles > 0) {
+      if (grp == 0) load_k(0); else load_v(0);
+    }
+  } else if (grp == 1) {
     if (n_tiles > 0) load_k(0);
     if (n_tiles > 1) load_k(1);
   }
@@ -370,6 +388,75 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_bf16_kernel(
       step_body(grp_c, std::integral_constant<int, 1>{}, step + 1);
     }
   };
+  // Row groups: both groups walk every tile, group 1 one phase behind group 0
+  // (each group on its own rows, so the softmax of one and the MFMAs of the
+  // other still alternate on every SIMD).
+  //   step s   phase A                        | phase B
+  //   group 0: P.V s-1, scores s               | copy V s+1; softmax s
+  //   group 1: copy K s+1; softmax s-1         | P.V s-1, scores s
+  // K s and V s live in slot s % 4. Group 1 waits for K s+1 at the end of
+  // step s, group 0 for V s+1 at the end of phase A of step s+1; each slot
+  // is refilled three steps after its last read.
+  auto step_rows = [&](auto grp_c, auto s4_c, int s) __attribute__((always_inline)) {
+    constexpr int GRP = decltype(grp_c)::value;
+    constexpr int S4 = decltype(s4_c)::value;
+    constexpr int KB = S4 * L::TILE_BYTES;
+    constexpr int VB = ((S4 + 3) % 4) * L::TILE_BYTES;
+    if constexpr (GRP == 0) {
+      if (s > 0 && s - 1 < n_vis) pv(p, std::integral_constant<int, VB>{});
+      if (s < n_vis) score(sc, std::integral_constant<int, KB>{});
+      wait_vmcnt0();
+      __syncthreads();
+      if (s + 1 < n_tiles) load_v(s + 1);
+      if (s < n_vis) softmax(sc, p, s);
+      __syncthreads();
+    } else {
+      if (s + 1 < n_tiles) load_k(s + 1);
+      const bool prev = s > 0 && s - 1 < n_vis;
+      if (prev) softmax(sc, p, s - 1);
+      __syncthreads();
+      if (prev) pv(p, std::integral_constant<int, VB>{});
+      if (s < n_vis) score(sc, std::integral_constant<int, KB>{});
+      wait_vmcnt0();
+      __syncthreads();
+    }
+  };
+  auto run_rows = [&](auto grp_c) __attribute__((always_inline)) {
+    for (int s = 0; s <= n_tiles; s += 4) {
+      step_rows(grp_c, std::integral_constant<int, 0>{}, s);
+      if (s + 1 > n_tiles) break;
+      step_rows(grp_c, std::integral_constant<int, 1>{}, s + 1);
+      if (s + 2 > n_tiles) break;
+      step_rows(grp_c, std::integral_constant<int, 2>{}, s + 2);
+      if (s + 3 > n_tiles) break;
+      step_rows(grp_c, std::integral_constant<int, 3>{}, s + 3);
+    }
+  };
+  if constexpr (ROWG) {
+    if (grp == 0) {
+      run_rows(std::integral_constant<int, 0>{});
+    } else {
+      run_rows(std::integral_constant<int, 1>{});
+    }
+    wait_vmcnt0();
+    // Each wave holds whole rows: normalise and store.
+    if (qrow < Nq) {
+      const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+      uint16_t* orow = O + ((size_t)bh * Nq + qrow) * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int d = db * 32 + i4 * 8 + hl * 4;
+          u32x2 w;
+          w[0] = pack_bf16x2(o[db][i4 * 4] * inv, o[db][i4 * 4 + 1] * inv);
+          w[1] = pack_bf16x2(o[db][i4 * 4 + 2] * inv, o[db][i4 * 4 + 3] * inv);
+          *reinterpret_cast<u32x2*>(orow + d) = w;
+        }
+      if (lane < 32) LSE[(size_t)bh * Nq + qrow] = l_run > 0.f ? (m_run + fast_log2(l_run)) * kLn2 : kNegInf;
+    }
+    return;
+  }
   if (grp == 0) {
     run(std::integral_constant<int, 0>{});
   } else {
@@ -441,22 +528,45 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_bf16_kernel(
   }
 }
 
+// Row groups are used when the grid of 256-row blocks has at least this many
+// workgroups (one per CU).
+constexpr long kRowGroupsMinWg = 256;
+
 template <int D>
 hipError_t launch_fwd_bf16_d(const FwdArgs& a) {
+  {
+    // Row groups (256 rows per workgroup) when the grid still fills the chip.
+    const int n_qt2 = (a.Nq + 2 * kFwdBM - 1) / (2 * kFwdBM);
+    const bool paired = a.causal && n_qt2 >= 2;
+    const long n_wg2 = (long)a.B * a.Hq * (paired ? (n_qt2 + 1) / 2 : n_qt2);
+    if (n_wg2 >= kRowGroupsMinWg) {
+      const float sl2 = a.scale * kLog2e;
+      if (paired) {
+        hipLaunchKernelGGL((fwd_bf16_kernel<D, true, true>), dim3((unsigned)n_wg2), dim3(kFwdThreads), 0,
+                           (hipStream_t)a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                           (uint16_t*)a.o, a.lse, a.Hq, a.Hkv, a.Nq, a.Nk, sl2, a.causal, n_qt2, (int)n_wg2);
+      } else {
+        hipLaunchKernelGGL((fwd_bf16_kernel<D, false, true>), dim3((unsigned)n_wg2), dim3(kFwdThreads), 0,
+                           (hipStream_t)a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                           (uint16_t*)a.o, a.lse, a.Hq, a.Hkv, a.Nq, a.Nk, sl2, a.causal, n_qt2, (int)n_wg2);
+      }
+      return hipGetLastError();
+    }
+  }
   const int n_qt = (a.Nq + kFwdBM - 1) / kFwdBM;
   const float sl2 = a.scale * kLog2e;
   // Causal with at least two query blocks per head: paired blocks.
   if (a.causal && n_qt >= 2) {
     const long n_wg = (long)a.B * a.Hq * ((n_qt + 1) / 2);
     if (n_wg == 0) return hipSuccess;
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, true>), dim3((unsigned)n_wg), dim3(kFwdThreads), 0,
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, true, false>), dim3((unsigned)n_wg), dim3(kFwdThreads), 0,
                        (hipStream_t)a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                        (uint16_t*)a.o, a.lse, a.Hq, a.Hkv, a.Nq, a.Nk, sl2, a.causal, n_qt, (int)n_wg);
     return hipGetLastError();
   }
   const long n_wg = (long)a.B * a.Hq * n_qt;
   if (n_wg == 0) return hipSuccess;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, false>), dim3((unsigned)n_wg), dim3(kFwdThreads), 0, (hipStream_t)a.stream,
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, false, false>), dim3((unsigned)n_wg), dim3(kFwdThreads), 0, (hipStream_t)a.stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse,
                      a.Hq, a.Hkv, a.Nq, a.Nk, sl2, a.causal, n_qt, (int)n_wg);
   return hipGetLastError();

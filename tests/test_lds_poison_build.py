@@ -1,5 +1,5 @@
 """The LDS-poisoning debug build (host only): compiled with FA_LDS_POISON, the
-forward kernels store all-ones to each copy's LDS destination right before the
+forward kernels (bf16 at every head size, fp8) store all-ones to each copy's LDS destination right before the
 copy is issued; the regular build has no such stores."""
 import os
 import re
@@ -10,8 +10,11 @@ import pytest
 from exact_io_aware_17_amd import build as B
 
 
-def _asm(extra):
-    src = os.path.join(B.CSRC, "fa_fwd.hip")
+SOURCES = ["fa_fwd.hip", "fa_fwd_wide.hip", "fa_fwd_fp8.hip"]
+
+
+def _asm(src, extra):
+    src = os.path.join(B.CSRC, src)
     r = subprocess.run([B.hipcc(), *B.HIP_FLAGS, *extra, "--cuda-device-only", "-S", src, "-o", "-"],
                        capture_output=True, text=True)
     if r.returncode:
@@ -36,11 +39,13 @@ def _poisoned_copies(asm):
     return n_copy, n_poisoned
 
 
-def test_poison_build_stores_before_every_copy():
-    n, p = _poisoned_copies(_asm(["-DFA_LDS_POISON"]))
+@pytest.mark.parametrize("src", SOURCES)
+def test_poison_build_stores_before_every_copy(src):
+    n, p = _poisoned_copies(_asm(src, ["-DFA_LDS_POISON"]))
     assert n > 0 and p == n, (n, p)
 
 
-def test_regular_build_has_no_poison_stores():
-    n, p = _poisoned_copies(_asm([]))
+@pytest.mark.parametrize("src", SOURCES)
+def test_regular_build_has_no_poison_stores(src):
+    n, p = _poisoned_copies(_asm(src, []))
     assert n > 0 and p == 0, (n, p)

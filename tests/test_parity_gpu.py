@@ -58,6 +58,32 @@ def test_bf16_full_oracle(w):
     assert_close(errors(o, o_ref, lse, lse_ref), what=w.name)
 
 
+# Grids of at least 256 blocks of 256 query rows (pairs of blocks under the
+# causal mask) take the row-group layout of the d = 64/128 kernel (both wave
+# groups on their own rows, every KV tile): many small heads keep the oracle
+# cheap while the launch uses that layout.
+ROW_GROUPS = [
+    synth.Workload("rows_ragged_gqa", 2, 128, 32, 200, 333, 128, seed=21),
+    # 3 blocks per head: pairs (2, 0) and the middle block 1 alone.
+    synth.Workload("rows_ragged_gqa_causal_odd_blocks", 2, 128, 32, 600, 650, 128, causal=True, seed=22),
+    # Nq > Nk under the mask: the first rows see no key.
+    synth.Workload("rows_more_queries_than_keys_causal", 1, 256, 64, 300, 70, 128, causal=True, seed=23),
+    synth.Workload("rows_causal_d64", 1, 256, 64, 257, 257, 64, causal=True, seed=24),
+    synth.Workload("rows_d64_long_keys", 1, 256, 256, 100, 1000, 64, seed=25),
+    synth.Workload("rows_keys_below_one_tile", 1, 256, 128, 256, 17, 128, seed=26),
+    # One query per head: seven of the eight waves hold no row.
+    synth.Workload("rows_one_query", 4, 64, 16, 1, 1000, 128, seed=27),
+]
+
+
+@pytest.mark.parametrize("w", ROW_GROUPS, ids=lambda w: w.name)
+def test_bf16_row_groups_full_oracle(w):
+    say(f"case bf16 row groups {w.name}")
+    o, lse = _run_fwd(w)
+    o_ref, lse_ref = oracle_full(w)
+    assert_close(errors(o, o_ref, lse, lse_ref), what=w.name)
+
+
 def _random_shapes(n=24, seed=2027):
     """Seeded mixed shapes: batch 1-2, 1-3 KV heads, GQA 1/2/4, 1..399 rows and
     keys, d 64, 128 or 256, with and without causal."""
