@@ -133,7 +133,17 @@ def bench_prefill(w, steps, warmup, device, min_warm_s=0.2):
         fa.fa_fwd(q, k, v, o, lse, scale=w.scale, causal=w.causal)
     wall, ev_ms = time_steps(step, steps, warmup, min_warm_s)
     return {"wall_s": wall, "ms_per_step": wall * 1e3 / steps, "kernel_ms": ev_ms,
-            "tflops": w.flops() / (wall / steps) / 1e12, "kernel_tflops": w.flops() / (ev_ms * 1e-3) / 1e12}
+            "tflops": w.flops() / (wall / steps) / 1e12, "kernel_tflops": w.flops() / (ev_ms * 1e-3) / 1e12,
+            "layout": fa.fa_fwd_layout(w.B, w.Hq, w.Nq, w.d, w.causal)}
+
+
+def fwd_kernel_label(w, layout):
+    """The kernel instance fa_fwd launches for workload w in `layout`."""
+    if layout.startswith("wide"):
+        return f"fwd_bf16_wide_kernel<{w.d}, {1 if layout == 'wide_one_group' else 2}>"
+    paired = "true" if layout.endswith("paired") else "false"
+    rows = "true" if layout.startswith("rows") else "false"
+    return f"fwd_bf16_kernel<{w.d}, {paired}, {rows}>"
 
 
 def bench_prefill_fp8(w, steps, warmup, device, min_warm_s=0.2):
@@ -489,7 +499,7 @@ def main():
                          "unit": "TFLOP/s", "frac": round(r["kernel_tflops"] / PEAK_BF16_TFLOPS, 4),
                          "traffic": traffic_from_profile(f"fwd_bf16_{name}_traffic.md", FWD_SOURCES),
                          "kernel_ms": round(r["kernel_ms"], 5),
-                         "kernel": "fwd_bf16_kernel<64>" if w.d == 64 else "fwd_bf16_kernel<128>"}}
+                         "kernel": fwd_kernel_label(w, r["layout"]), "layout": r["layout"]}}
     log("sustained shader clock ...")
     wsc = synth.WORKLOADS[PREFILL]
     import exact_io_aware_17_amd as fa
@@ -523,7 +533,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(rp["kernel_tflops"], 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(rp["kernel_tflops"] / PEAK_BF16_TFLOPS, 4),
                      "traffic": fwd_traffic, "kernel_ms": round(rp["kernel_ms"], 5),
-                     "kernel": "fwd_bf16_kernel<128>"},
+                     "kernel": fwd_kernel_label(wp, rp["layout"]), "layout": rp["layout"]},
         "prefill_fp8": {"workload": w8.name, "dtype": "fp8 e4m3 (per-tensor descale), bf16 out",
                         "metric": "attention fwd TFLOPS (4*B*H*Nq*Nk*d per forward)", "value": round(r8["tflops"], 2),
                         "unit": "TFLOP/s", "ms_per_step": round(r8["ms_per_step"], 5),

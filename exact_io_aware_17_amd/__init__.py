@@ -31,6 +31,7 @@ STATUS_NAMES = {0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_UNSU
 _P, _I, _F, _S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
 SIGNATURES = {
     "fa_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "fa_fwd_layout": (_I, [_I, _I, _I, _I, _I]),
     "fa_fwd_fp32": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P]),
     "fa_fwd_fp8": (_I, [_P, _P, _P, _F, _F, _F, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P]),
     "fa_bwd_workspace_bytes": (_S, [_I, _I, _I, _I]),
@@ -145,6 +146,16 @@ def _out_check(o, lse, q, odtype):
         raise ValueError("o must be a contiguous tensor shaped like q")
     if lse.dtype != torch.float32 or tuple(lse.shape) != tuple(q.shape[:3]) or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 [B, Hq, Nq] tensor")
+
+
+# fa_fwd's work layouts (FA_LAYOUT_* in fa.h).
+LAYOUT_NAMES = {0: "kv_parity", 1: "kv_parity_paired", 2: "rows", 3: "rows_paired", 4: "wide_one_group",
+                5: "wide_two_groups"}
+
+
+def fa_fwd_layout(B, Hq, Nq, d, causal) -> str:
+    """Name of the work layout fa_fwd uses for this shape."""
+    return LAYOUT_NAMES.get(int(lib().fa_fwd_layout(B, Hq, Nq, d, int(bool(causal)))), "unsupported")
 
 
 def fa_fwd(q, k, v, o, lse, scale=None, causal=False, stream=None):

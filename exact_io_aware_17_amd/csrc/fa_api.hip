@@ -141,6 +141,18 @@ const char* fa_status_str(fa_status s) {
   return "unknown fa_status";
 }
 
+static_assert(fa::kLayoutKvParity == FA_LAYOUT_KV_PARITY && fa::kLayoutKvParityPaired == FA_LAYOUT_KV_PARITY_PAIRED &&
+                  fa::kLayoutRows == FA_LAYOUT_ROWS && fa::kLayoutRowsPaired == FA_LAYOUT_ROWS_PAIRED &&
+                  fa::kLayoutWideOneGroup == FA_LAYOUT_WIDE_ONE_GROUP &&
+                  fa::kLayoutWideTwoGroups == FA_LAYOUT_WIDE_TWO_GROUPS,
+              "layout numbers must match the header");
+
+int fa_fwd_layout(int B, int Hq, int Nq, int d, int causal) {
+  if (d == 64 || d == 128) return fa::plan_fwd_bf16(B, Hq, Nq, causal ? 1 : 0).layout;
+  if (d == 192 || d == 256) return fa::fwd_wide_layout(B, Hq, Nq);
+  return -1;
+}
+
 fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
                  int Nq, int Nk, int d, float scale, int causal, void* stream) {
   fa_status st = check_common(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal);

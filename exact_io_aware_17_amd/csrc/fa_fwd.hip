@@ -532,43 +532,24 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_bf16_kernel(
 // workgroups (one per CU).
 constexpr long kRowGroupsMinWg = 256;
 
+template <int D, bool PAIRED, bool ROWG>
+void launch_one(const FwdArgs& a, const FwdPlan& pl) {
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, PAIRED, ROWG>), dim3((unsigned)pl.n_wg), dim3(kFwdThreads), 0,
+                     (hipStream_t)a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                     (uint16_t*)a.o, a.lse, a.Hq, a.Hkv, a.Nq, a.Nk, a.scale * kLog2e, a.causal, pl.n_qt,
+                     (int)pl.n_wg);
+}
+
 template <int D>
 hipError_t launch_fwd_bf16_d(const FwdArgs& a) {
-  {
-    // Row groups (256 rows per workgroup) when the grid still fills the chip.
-    const int n_qt2 = (a.Nq + 2 * kFwdBM - 1) / (2 * kFwdBM);
-    const bool paired = a.causal && n_qt2 >= 2;
-    const long n_wg2 = (long)a.B * a.Hq * (paired ? (n_qt2 + 1) / 2 : n_qt2);
-    if (n_wg2 >= kRowGroupsMinWg) {
-      const float sl2 = a.scale * kLog2e;
-      if (paired) {
-        hipLaunchKernelGGL((fwd_bf16_kernel<D, true, true>), dim3((unsigned)n_wg2), dim3(kFwdThreads), 0,
-                           (hipStream_t)a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                           (uint16_t*)a.o, a.lse, a.Hq, a.Hkv, a.Nq, a.Nk, sl2, a.causal, n_qt2, (int)n_wg2);
-      } else {
-        hipLaunchKernelGGL((fwd_bf16_kernel<D, false, true>), dim3((unsigned)n_wg2), dim3(kFwdThreads), 0,
-                           (hipStream_t)a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                           (uint16_t*)a.o, a.lse, a.Hq, a.Hkv, a.Nq, a.Nk, sl2, a.causal, n_qt2, (int)n_wg2);
-      }
-      return hipGetLastError();
-    }
+  const FwdPlan pl = plan_fwd_bf16(a.B, a.Hq, a.Nq, a.causal);
+  if (pl.n_wg == 0) return hipSuccess;
+  switch (pl.layout) {
+    case kLayoutRows: launch_one<D, false, true>(a, pl); break;
+    case kLayoutRowsPaired: launch_one<D, true, true>(a, pl); break;
+    case kLayoutKvParityPaired: launch_one<D, true, false>(a, pl); break;
+    default: launch_one<D, false, false>(a, pl); break;
   }
-  const int n_qt = (a.Nq + kFwdBM - 1) / kFwdBM;
-  const float sl2 = a.scale * kLog2e;
-  // Causal with at least two query blocks per head: paired blocks.
-  if (a.causal && n_qt >= 2) {
-    const long n_wg = (long)a.B * a.Hq * ((n_qt + 1) / 2);
-    if (n_wg == 0) return hipSuccess;
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, true, false>), dim3((unsigned)n_wg), dim3(kFwdThreads), 0,
-                       (hipStream_t)a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                       (uint16_t*)a.o, a.lse, a.Hq, a.Hkv, a.Nq, a.Nk, sl2, a.causal, n_qt, (int)n_wg);
-    return hipGetLastError();
-  }
-  const long n_wg = (long)a.B * a.Hq * n_qt;
-  if (n_wg == 0) return hipSuccess;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, false, false>), dim3((unsigned)n_wg), dim3(kFwdThreads), 0, (hipStream_t)a.stream,
-                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse,
-                     a.Hq, a.Hkv, a.Nq, a.Nk, sl2, a.causal, n_qt, (int)n_wg);
   return hipGetLastError();
 }
 
@@ -576,6 +557,16 @@ hipError_t launch_fwd_bf16_d(const FwdArgs& a) {
 
 hipError_t launch_fwd_bf16(const FwdArgs& a) {
   return a.d == 128 ? launch_fwd_bf16_d<128>(a) : launch_fwd_bf16_d<64>(a);
+}
+
+FwdPlan plan_fwd_bf16(int B, int Hq, int Nq, int causal) {
+  const int n_qt2 = (Nq + 2 * kFwdBM - 1) / (2 * kFwdBM);
+  const bool paired2 = causal && n_qt2 >= 2;
+  const long n_wg2 = (long)B * Hq * (paired2 ? (n_qt2 + 1) / 2 : n_qt2);
+  if (n_wg2 >= kRowGroupsMinWg) return {paired2 ? kLayoutRowsPaired : kLayoutRows, n_qt2, n_wg2};
+  const int n_qt = (Nq + kFwdBM - 1) / kFwdBM;
+  if (causal && n_qt >= 2) return {kLayoutKvParityPaired, n_qt, (long)B * Hq * ((n_qt + 1) / 2)};
+  return {kLayoutKvParity, n_qt, (long)B * Hq * n_qt};
 }
 
 long fwd_bf16_grid(int B, int Hq, int Nq) { return (long)B * Hq * ((Nq + kFwdBM - 1) / kFwdBM); }

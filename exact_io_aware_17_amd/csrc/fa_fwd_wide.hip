@@ -387,6 +387,11 @@ hipError_t launch_wide_d(const FwdArgs& a) {
 
 }  // namespace
 
+int fwd_wide_layout(int B, int Hq, int Nq) {
+  const long n_wg = (long)B * Hq * ((Nq + k2BM - 1) / k2BM);
+  return n_wg >= kWideOneGroupMinWg ? kLayoutWideOneGroup : kLayoutWideTwoGroups;
+}
+
 hipError_t launch_fwd_bf16_wide(const FwdArgs& a) {
   return a.d == 256 ? launch_wide_d<256>(a) : launch_wide_d<192>(a);
 }

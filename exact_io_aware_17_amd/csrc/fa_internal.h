@@ -18,6 +18,23 @@ struct FwdArgs {
   void* stream;
 };
 
+// Work layouts of the bf16 prefill (the numbers are the FA_LAYOUT_* values of
+// the public header).
+enum FwdLayoutKind {
+  kLayoutKvParity = 0,        // 128 rows, KV-parity wave groups
+  kLayoutKvParityPaired = 1,  // same, causal pairs of query blocks
+  kLayoutRows = 2,            // 256 rows, row groups
+  kLayoutRowsPaired = 3,      // same, causal pairs
+  kLayoutWideOneGroup = 4,    // d = 192/256: 4 waves, two workgroups per CU
+  kLayoutWideTwoGroups = 5,   // d = 192/256: 8 waves, KV-parity groups
+};
+
+struct FwdPlan {
+  int layout;  // FwdLayoutKind
+  int n_qt;    // query blocks per head in the layout's block size
+  long n_wg;   // workgroups
+};
+
 struct SplitArgs {
   FwdArgs f;
   int num_splits;
@@ -52,6 +69,8 @@ struct BwdArgs {
 };
 
 hipError_t launch_fwd_bf16(const FwdArgs& a);       // d = 64, 128
+FwdPlan plan_fwd_bf16(int B, int Hq, int Nq, int causal);
+int fwd_wide_layout(int B, int Hq, int Nq);
 hipError_t launch_fwd_bf16_wide(const FwdArgs& a);  // d = 192, 256
 hipError_t launch_fwd_fp32(const FwdArgs& a);
 // q, k, v of `a` are E4M3 bytes (d = 128); o is bf16, lse fp32.

@@ -72,6 +72,22 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
                  int B, int Hq, int Hkv, int Nq, int Nk, int d,
                  float scale, int causal, void* stream);
 
+/* Work layouts of fa_fwd, as reported by fa_fwd_layout. */
+#define FA_LAYOUT_KV_PARITY 0        /* 128 query rows per workgroup, KV tiles alternate between two wave groups */
+#define FA_LAYOUT_KV_PARITY_PAIRED 1 /* the same, causal: query blocks n-1-p and p per workgroup */
+#define FA_LAYOUT_ROWS 2             /* 256 query rows per workgroup, both wave groups over every KV tile */
+#define FA_LAYOUT_ROWS_PAIRED 3      /* the same, causal pairs */
+#define FA_LAYOUT_WIDE_ONE_GROUP 4   /* d = 192/256: 4 waves per 128 rows, two workgroups per CU */
+#define FA_LAYOUT_WIDE_TWO_GROUPS 5  /* d = 192/256: 8 waves per 128 rows, KV-parity groups */
+
+/*
+ * fa_fwd_layout -- the FA_LAYOUT_* value fa_fwd uses for this shape (the
+ * choice depends on the grid size only), or -1 for a head size fa_fwd does
+ * not take. Introspection for tests and benchmarks: no argument checks, no
+ * GPU work.
+ */
+int fa_fwd_layout(int B, int Hq, int Nq, int d, int causal);
+
 /*
  * fa_fwd_fp32 -- the same operation in fp32 throughout (debug / reference
  * path; plain FMA arithmetic, no matrix cores).  It computes the standard

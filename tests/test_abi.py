@@ -20,7 +20,7 @@ def _declarations():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     decls = {}
-    for m in re.finditer(r"^\s*(fa_status|size_t|float|const char\s*\*)\s*(fa_\w+)\s*\(([^)]*)\)\s*;", text,
+    for m in re.finditer(r"^\s*(fa_status|size_t|float|int|const char\s*\*)\s*(fa_\w+)\s*\(([^)]*)\)\s*;", text,
                          re.M | re.S):
         params = [p.strip() for p in m.group(3).split(",") if p.strip() and p.strip() != "void"]
         decls[m.group(2)] = (m.group(1), len(params))
@@ -32,7 +32,7 @@ def test_header_declarations_found():
     assert set(d) == {"fa_fwd", "fa_fwd_fp32", "fa_fwd_fp8", "fa_bwd", "fa_bwd_workspace_bytes",
                       "fa_splitkv_workspace_bytes", "fa_fwd_splitkv", "fa_fwd_splitkv_noalloc",
                       "fa_fwd_splitkv_paged", "fa_combine", "fa_status_str", "fa_default_scale",
-                      "fa_build_hash"}
+                      "fa_build_hash", "fa_fwd_layout"}
 
 
 def test_library_exports_every_declared_symbol():
@@ -51,6 +51,26 @@ def test_status_strings():
 
 def _fwd(entry="fa_fwd", q=P, k=P, v=P, o=P, lse=P, B=1, Hq=2, Hkv=1, Nq=16, Nk=16, d=128, scale=0.1, causal=0):
     return getattr(fa.lib(), entry)(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal, None)
+
+
+def test_forward_layouts():
+    """fa_fwd's layout follows the grid size: 256-row blocks (row groups)
+    once they fill the 256 CUs, 128-row KV-parity blocks below that, causal
+    pairs of blocks when a head has at least two; head sizes 192/256 have
+    their own kernel."""
+    L = fa.fa_fwd_layout
+    assert L(1, 8, 4096, 128, False) == "kv_parity"  # the pages' shape: 128 blocks of 256 rows
+    assert L(4, 16, 2048, 128, False) == "rows"  # 512 blocks
+    assert L(4, 16, 2048, 128, True) == "rows_paired"  # 4 x 16 x 4 pairs = 256
+    assert L(1, 32, 16384, 128, True) == "rows_paired"
+    assert L(1, 16, 2048, 128, True) == "kv_parity_paired"  # 64 pairs of 256-row blocks: too few
+    assert L(1, 1, 256, 64, False) == "kv_parity"
+    assert L(256, 1, 256, 64, False) == "rows"
+    assert L(1, 2, 384, 128, True) == "kv_parity_paired"
+    assert L(1, 2, 100, 128, True) == "kv_parity"  # one block per head: nothing to pair
+    assert L(1, 8, 4096, 256, False) == "wide_two_groups"
+    assert L(4, 16, 2048, 192, True) == "wide_one_group"
+    assert L(1, 8, 4096, 96, False) == "unsupported"
 
 
 @pytest.mark.parametrize("entry", ["fa_fwd", "fa_fwd_fp32"])

@@ -79,6 +79,7 @@ ROW_GROUPS = [
 @pytest.mark.parametrize("w", ROW_GROUPS, ids=lambda w: w.name)
 def test_bf16_row_groups_full_oracle(w):
     say(f"case bf16 row groups {w.name}")
+    assert _fa().fa_fwd_layout(w.B, w.Hq, w.Nq, w.d, w.causal).startswith("rows")
     o, lse = _run_fwd(w)
     o_ref, lse_ref = oracle_full(w)
     assert_close(errors(o, o_ref, lse, lse_ref), what=w.name)
@@ -169,10 +170,14 @@ def test_bf16_d256_full_size_sampled(name):
 @pytest.mark.parametrize("name", ["batched_prefill_b4h16_n2048", "batched_prefill_b4h16_n2048_causal",
                                   "pages_shape_h8_q4096_kv8192"])
 def test_bf16_full_size_every_element(name):
-    """Full-size launch (the configuration the benchmark times), every element
-    of every head against the oracle."""
+    """Full-size launch (the configuration the benchmark times: the pages'
+    shape in KV-parity blocks, the batched shapes in row groups), every
+    element of every head against the oracle."""
     w = W[name]
-    say(f"case bf16 full-size {name}, every head")
+    layout = _fa().fa_fwd_layout(w.B, w.Hq, w.Nq, w.d, w.causal)
+    assert layout == {"pages_shape_h8_q4096_kv8192": "kv_parity", "batched_prefill_b4h16_n2048": "rows",
+                      "batched_prefill_b4h16_n2048_causal": "rows_paired"}[name]
+    say(f"case bf16 full-size {name} ({layout}), every head")
     o, lse = _run_fwd(w)
     o_ref, lse_ref = oracle_full(w)
     for b in range(w.B):
