@@ -263,13 +263,15 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_bf16_kernel(
     // Probabilities against the current reference; returns the tile's row sum.
     auto exps = [&]() __attribute__((always_inline)) {
       const float neg_m = -m_run;
-      float rs[4] = {0.f, 0.f, 0.f, 0.f};
+      // Four partial row sums, each started from its first term (an add to
+      // 0.0 is not folded away: it would turn -0 into +0).
+      float rs[4];
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const float e = fast_exp2(__builtin_fmaf(sc[mb][i], sl2, neg_m));
-          rs[i & 3] += e;
+          rs[i & 3] = mb == 0 && i < 4 ? e : rs[i & 3] + e;
           p[mb][i >> 3][i & 7] = (__bf16)e;
         }
       return sum_with_lane_xor32((rs[0] + rs[1]) + (rs[2] + rs[3]));

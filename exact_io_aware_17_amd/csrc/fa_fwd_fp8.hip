@@ -236,16 +236,20 @@ __global__ __launch_bounds__(kF8Threads) void fwd_fp8_kernel(
     }
     auto exps = [&]() __attribute__((always_inline)) {
       const float neg_m = -m_run;
-      float rs[4] = {0.f, 0.f, 0.f, 0.f};
+      float rs[4];  // each started from its first term (see the bf16 kernel)
 #pragma unroll
       for (int w = 0; w < 8; ++w) {
         float e[4];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           e[c] = fast_exp2(__builtin_fmaf(sc[w >> 2][(w & 3) * 4 + c], sl2, neg_m));
-          rs[c] += e[c];
+          rs[c] = w == 0 ? e[c] : rs[c] + e[c];
         }
-        int v = __builtin_amdgcn_cvt_pk_fp8_f32(e[0], e[1], 0, false);
+        // The first conversion writes bytes 0-1 and keeps bytes 2-3 of its
+        // third operand, which the second then overwrites: passing the old
+        // pk[w] (already consumed by the previous P.V) spares zeroing a
+        // register per word.
+        int v = __builtin_amdgcn_cvt_pk_fp8_f32(e[0], e[1], pk[w], false);
         pk[w] = __builtin_amdgcn_cvt_pk_fp8_f32(e[2], e[3], v, true);
       }
       return sum_with_lane_xor32((rs[0] + rs[1]) + (rs[2] + rs[3]));
@@ -310,7 +314,7 @@ __global__ __launch_bounds__(kF8Threads) void fwd_fp8_kernel(
   //   group 0: P.V 2s-2, scores 2s                 | copy K 2s+3, V 2s+1; softmax 2s
   //   group 1: copy K 2s+2, V 2s; softmax 2s-1     | P.V 2s-1, scores 2s+1
   f32x16 sc[2];
-  i32x8 pk;
+  i32x8 pk = i32x8{};
   auto step_body = [&](auto grp_c, auto par_c, int step) __attribute__((always_inline)) {
     constexpr int GRP = decltype(grp_c)::value;
     constexpr int PAR = decltype(par_c)::value;

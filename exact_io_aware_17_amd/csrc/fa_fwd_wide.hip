@@ -231,11 +231,11 @@ __global__ __launch_bounds__(64 * k2WavesPerGroup * NG, 2 / NG) void fwd_bf16_wi
     bf16x8 p[2];
     auto exps = [&]() __attribute__((always_inline)) {
       const float neg_m = -m_run;
-      float rs[4] = {0.f, 0.f, 0.f, 0.f};
+      float rs[4];  // each started from its first term (see the d = 128 kernel)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const float e = fast_exp2(__builtin_fmaf(sc[i], sl2, neg_m));
-        rs[i & 3] += e;
+        rs[i & 3] = i < 4 ? e : rs[i & 3] + e;
         p[i >> 3][i & 7] = (__bf16)e;
       }
       return sum_with_lane_xor32((rs[0] + rs[1]) + (rs[2] + rs[3]));
