@@ -251,13 +251,17 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_bf16_kernel(
     const int kv0 = t * BN;
     const bool need_mask = (kv0 + BN > Nk) || (causal && kv0 + BN - 1 > qw0 + diag);
     if (need_mask) {
-      const int lim = causal ? qrow + diag : 0x7fffffff;
+      // Key kv0 + c + 8 hl (c the register's offset, score_key) is visible
+      // iff it is at most L = min(last key, the row's causal limit): one
+      // per-lane bound, then a compare with a constant per score.
+      const int L = causal && qrow + diag < Nk - 1 ? qrow + diag : Nk - 1;
+      const int t = L - kv0 - 8 * hl;
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int key = kv0 + score_key(mb * 32, i, lane);
-          if (key >= Nk || key > lim) sc[mb][i] = kNegInf;
+          const int c = score_key(mb * 32, i, 0);
+          if (c > t) sc[mb][i] = kNegInf;
         }
     }
     // Probabilities against the current reference; returns the tile's row sum.

@@ -225,14 +225,16 @@ __global__ __launch_bounds__(kF8Threads) void fwd_fp8_kernel(
     const int kv0 = t * BN;
     const bool need_mask = (kv0 + BN > Nk) || (causal && kv0 + BN - 1 > qw0 + diag);
     if (need_mask) {
-      const int lim = causal ? qrow + diag : 0x7fffffff;
+      // Key kv0 + c + 4 hl is visible iff it is at most L = min(last key, the
+      // row's causal limit): one per-lane bound, a compare with a constant
+      // per score.
+      const int L = causal && qrow + diag < Nk - 1 ? qrow + diag : Nk - 1;
+      const int t = L - kv0 - 4 * hl;
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = kv0 + mb * 32 + (i >> 2) * 8 + hl * 4 + (i & 3);
-          if (key >= Nk || key > lim) sc[mb][i] = kNegInf;
-        }
+        for (int i = 0; i < 16; ++i)
+          if (mb * 32 + (i >> 2) * 8 + (i & 3) > t) sc[mb][i] = kNegInf;
     }
     auto exps = [&]() __attribute__((always_inline)) {
       const float neg_m = -m_run;

@@ -221,12 +221,13 @@ __global__ __launch_bounds__(64 * k2WavesPerGroup * NG, 2 / NG) void fwd_bf16_wi
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     const int kv0 = t * BN;
     if ((kv0 + BN > Nk) || (causal && kv0 + BN - 1 > qw0 + diag)) {
-      const int lim = causal ? qrow + diag : 0x7fffffff;
+      // One per-lane bound, then a compare with a constant per score (see
+      // the d = 128 kernel).
+      const int L = causal && qrow + diag < Nk - 1 ? qrow + diag : Nk - 1;
+      const int t = L - kv0 - 8 * hl;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = kv0 + score_key(0, i, lane);
-        if (key >= Nk || key > lim) sc[i] = kNegInf;
-      }
+      for (int i = 0; i < 16; ++i)
+        if (score_key(0, i, 0) > t) sc[i] = kNegInf;
     }
     bf16x8 p[2];
     auto exps = [&]() __attribute__((always_inline)) {
