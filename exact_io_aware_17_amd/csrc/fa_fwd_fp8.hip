@@ -305,6 +305,7 @@ __global__ __launch_bounds__(kF8Threads) void fwd_fp8_kernel(
   if (grp == 1) {
     if (n_tiles > 0) load_k(0);
     if (n_tiles > 1) load_k(1);
+    if (n_tiles > 0) load_v(0);
   }
   wait_vmcnt0();
 #pragma unroll
@@ -312,11 +313,24 @@ __global__ __launch_bounds__(kF8Threads) void fwd_fp8_kernel(
   __syncthreads();
 
   // Two-phase ping-pong, as in the bf16 kernel:
-  //   step s   phase A                           | phase B
-  //   group 0: P.V 2s-2, scores 2s                 | copy K 2s+3, V 2s+1; softmax 2s
-  //   group 1: copy K 2s+2, V 2s; softmax 2s-1     | P.V 2s-1, scores 2s+1
+  //   step s   phase A                                | phase B
+  //   group 0: P.V 2s-2, scores 2s; copy V 2s+1         | copy K 2s+3; softmax 2s
+  //   group 1: copy K 2s+2; softmax 2s-1                | P.V 2s-1, scores 2s+1; copy V 2s+2
+  // With 8-bit operands the MFMA phase (8 MFMAs per wave) is shorter than the
+  // softmax phase, so the V copies are issued by the MFMA wave after its
+  // MFMAs, one phase earlier than the K copies of the same tile step; each
+  // MFMA phase then waits for every copy except the V copies it just issued
+  // (those land a full step before P.V reads them). A V slot is rewritten only
+  // after the P.V of the tile four back, which ran in an earlier phase.
   f32x16 sc[2];
   i32x8 pk = i32x8{};
+  auto wait_all_but_v = [&](bool v_issued) __attribute__((always_inline)) {
+    if (v_issued) {
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kF8Copies) : "memory");
+    } else {
+      wait_vmcnt0();
+    }
+  };
   auto step_body = [&](auto grp_c, auto par_c, int step) __attribute__((always_inline)) {
     constexpr int GRP = decltype(grp_c)::value;
     constexpr int PAR = decltype(par_c)::value;
@@ -324,21 +338,23 @@ __global__ __launch_bounds__(kF8Threads) void fwd_fp8_kernel(
     if constexpr (GRP == 0) {
       if (step > 0 && t0 - 2 < n_vis) pv(pk, std::integral_constant<int, 2 * (1 - PAR) * kF8Tile>{});
       if (t0 < n_vis) score(sc, std::integral_constant<int, 2 * PAR * kF8Tile>{});
-      wait_vmcnt0();
+      const bool v_issued = t0 + 1 < n_tiles;
+      if (v_issued) load_v(t0 + 1);
+      wait_all_but_v(v_issued);
       __syncthreads();
       if (t0 + 3 < n_tiles) load_k(t0 + 3);
-      if (t0 + 1 < n_tiles) load_v(t0 + 1);
       if (t0 < n_vis) softmax(sc, pk, t0);
       __syncthreads();
     } else {
       if (t0 + 2 < n_tiles) load_k(t0 + 2);
-      if (t0 < n_tiles) load_v(t0);
       const bool prev = step > 0 && t0 - 1 < n_vis;
       if (prev) softmax(sc, pk, t0 - 1);
       __syncthreads();
       if (prev) pv(pk, std::integral_constant<int, (2 * (1 - PAR) + 1) * kF8Tile>{});
       if (t0 + 1 < n_vis) score(sc, std::integral_constant<int, (2 * PAR + 1) * kF8Tile>{});
-      wait_vmcnt0();
+      const bool v_issued = t0 + 2 < n_tiles;
+      if (v_issued) load_v(t0 + 2);
+      wait_all_but_v(v_issued);
       __syncthreads();
     }
   };
