@@ -52,6 +52,13 @@
 //  * Causal: tiles past the workgroup's last visible key are never loaded; a
 //    wave skips the math of tiles its rows cannot see; only tiles that cross
 //    the diagonal or the ragged end are masked element-wise.
+//  * Q and O move through LDS: each wave copies its 32 Q rows into LDS with
+//    the tile copies and reads them back as B operands, and stages its O rows
+//    there before storing them. Either way every global access instruction
+//    covers whole rows; accessing the rows straight from the MFMA layout
+//    would touch 32 rows with 8 or 16 bytes each per instruction, and with
+//    eight waves doing so at once the CU's address unit holds up the
+//    workgroup's first and last microseconds.
 //  * Workgroups are renumbered so that the query blocks of one head run on one
 //    XCD (its L2 then serves that head's K/V to all of them). Under the causal
 //    mask a workgroup takes the pair of query blocks n - 1 - p and p, so that
@@ -111,6 +118,44 @@ __device__ __forceinline__ void tile_to_lds(uint32_t slot_lds, const uint16_t* s
   }
 }
 
+// Stores of one wave's 32 rows of O through a wave-private LDS area. The
+// O^T accumulator gives lane l row l % 32 and, per (d block db, group i4),
+// the four columns 32 db + 8 i4 + 4 (l / 32) .. +3: a direct store would
+// write 8 bytes into each of 32 rows per instruction. Written to LDS in that
+// layout and read back row-major, every 16-byte-per-lane store covers whole
+// rows (4 rows at d = 128, 8 at d = 64), so the CU's address unit handles a
+// quarter of the pieces. Rows are padded by 16 bytes: the 8-byte writes of
+// one instruction then fall on at most two lanes per bank, the 16-byte reads
+// on distinct banks.
+template <int D>
+struct OStage {
+  static constexpr int RS = 2 * D + 16;   // padded row stride in bytes
+  static constexpr int BYTES = 32 * RS;   // one wave's area
+  static constexpr int LPR = 2 * D / 16;  // lanes per row of the read-back
+  static constexpr int RPS = 64 / LPR;    // rows per store instruction
+};
+
+// Column group (db, i4) of this lane's row into the staging area.
+template <int D>
+__device__ __forceinline__ void stage_o_cols(char* stage, int db, int i4, u32x2 w, int lane) {
+  *reinterpret_cast<u32x2*>(stage + (lane & 31) * OStage<D>::RS + (db * 32 + i4 * 8 + (lane >> 5) * 4) * 2) = w;
+}
+
+// The staged rows to global memory, whole rows per instruction; rows at or
+// past `nvalid` are not written.
+template <int D>
+__device__ __forceinline__ void store_o_staged(const char* stage, uint16_t* o_row0, int nvalid, int lane) {
+  using S = OStage<D>;
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int j = 0; j < 32 / S::RPS; ++j) {
+    const int r = j * S::RPS + lane / S::LPR;
+    const int c = (lane % S::LPR) * 16;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(stage + r * S::RS + c);
+    if (r < nvalid) *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(o_row0) + (size_t)r * 2 * D + c) = v;
+  }
+}
+
 // PAIRED (causal only): each workgroup takes query blocks n_qt - 1 - p and p of
 // one head, one after the other, so that every workgroup has the same number
 // of visible key tiles ((BM / 64) (n_qt + 1) per pair, instead of
@@ -152,11 +197,6 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_bf16_kernel(
   const int diag = Nk - Nq;  // key j visible to row i iff j <= i + diag
 
   bf16x8 qf[KS];
-#pragma unroll
-  for (int s = 0; s < KS; ++s) {
-    qf[s] = qrow < Nq ? *reinterpret_cast<const bf16x8*>(Qh + (size_t)qrow * D + s * 16 + hl * 8) : bf16x8{};
-  }
-
   // Loop-invariant per-lane LDS byte offsets (relative to `lds`); the slot
   // and the tile's row block are immediates.
   uint32_t koff[KS];
@@ -184,6 +224,31 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_bf16_kernel(
     goff[i] = (uint32_t)(row * D + swz<D>(row, lane % L::CH) * 8) * 2u;
   }
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(lds));
+  // Q rows of this wave go through a wave-private LDS area (K slots 2-3 for
+  // group 0, V slots 2-3 for group 1, which no copy fills before the first
+  // barrier of the loop), laid out as the first 32 rows of a K tile whose
+  // row r holds Q row kappa(r): each copy instruction fetches whole rows, and
+  // lane l then reads Q row l % 32 through the K operand offsets. Rows past
+  // Nq repeat row Nq - 1 (finite data whose results are not stored). The
+  // paired KV-parity layout loads Q straight into registers instead: its
+  // two items' code then fits 256 registers without spilling.
+  constexpr bool kQViaLds = ROWG || !PAIRED;
+  constexpr int QCOPIES = 32 * ROWB / 1024;
+  const uint32_t qstage = (grp == 0 ? 2 * L::TILE_BYTES : L::V_BASE + 2 * L::TILE_BYTES) + rw * 32 * ROWB;
+  if constexpr (kQViaLds) {
+#pragma unroll
+    for (int i = 0; i < QCOPIES; ++i) {
+      const int row = i * L::ROWS_PER_KB + lane / L::CH;
+      const int qr = qw0 + kappa(row);
+      const int grow = qr < Nq ? qr : Nq - 1;
+      dma16_sbase(Qh, (uint32_t)(grow * D + swz<D>(row, lane % L::CH) * 8) * 2u, lds0 + qstage + i * 1024);
+    }
+  } else {
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      qf[s] = qrow < Nq ? *reinterpret_cast<const bf16x8*>(Qh + (size_t)qrow * D + s * 16 + hl * 8) : bf16x8{};
+    }
+  }
 
   int kv_end = Nk;
   if (causal) {
@@ -337,6 +402,10 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_bf16_kernel(
     if (n_tiles > 1) load_k(1);
   }
   wait_vmcnt0();
+  if constexpr (kQViaLds) {
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(lds_c + qstage + koff[s]);
+  }
 #pragma unroll
   for (int s = 0; s < KS; ++s) asm volatile("" ::"v"(qf[s]));
   __syncthreads();
@@ -445,21 +514,24 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_bf16_kernel(
       run_rows(std::integral_constant<int, 1>{});
     }
     wait_vmcnt0();
-    // Each wave holds whole rows: normalise and store.
-    if (qrow < Nq) {
+    // Each wave holds whole rows: normalise and store. After the loop's last
+    // barrier no wave reads the tile slots any more, so each wave stages its
+    // rows in its own part of them.
+    {
       const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-      uint16_t* orow = O + ((size_t)bh * Nq + qrow) * D;
+      char* stage = reinterpret_cast<char*>(lds) + wave * OStage<D>::BYTES;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
-          const int d = db * 32 + i4 * 8 + hl * 4;
           u32x2 w;
           w[0] = pack_bf16x2(o[db][i4 * 4] * inv, o[db][i4 * 4 + 1] * inv);
           w[1] = pack_bf16x2(o[db][i4 * 4 + 2] * inv, o[db][i4 * 4 + 3] * inv);
-          *reinterpret_cast<u32x2*>(orow + d) = w;
+          stage_o_cols<D>(stage, db, i4, w, lane);
         }
-      if (lane < 32) LSE[(size_t)bh * Nq + qrow] = l_run > 0.f ? (m_run + fast_log2(l_run)) * kLn2 : kNegInf;
+      store_o_staged<D>(stage, O + ((size_t)bh * Nq + qw0) * D, Nq - qw0, lane);
+      if (lane < 32 && qrow < Nq)
+        LSE[(size_t)bh * Nq + qrow] = l_run > 0.f ? (m_run + fast_log2(l_run)) * kLn2 : kNegInf;
     }
     return;
   }
@@ -474,6 +546,9 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_bf16_kernel(
   // Merge the two groups (same rows, disjoint key sets) and write out.
   float* xo = reinterpret_cast<float*>(lds);                     // [4 rw][DB][16][64] fp32
   float* xm = reinterpret_cast<float*>(lds) + 4 * DB * 16 * 64;  // [4 rw][64] m, then [4 rw][64] l
+  constexpr int kMergeBytes = (4 * DB * 16 * 64 + 2 * 4 * 64) * 4;
+  static_assert(kMergeBytes + 4 * OStage<D>::BYTES <= (int)sizeof(lds), "merge and staging exceed LDS");
+  static_assert(8 * OStage<D>::BYTES <= (int)sizeof(lds), "row-group staging exceeds LDS");
   const float l_tot = l_run;  // already the total of both lane halves
   if (grp == 1) {
 #pragma unroll
@@ -493,26 +568,25 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_bf16_kernel(
     const float lsum = l_tot * a0 + l1 * a1;
     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
     const float c0 = a0 * inv, c1 = a1 * inv;
-    if (qrow < Nq) {
-      uint16_t* orow = O + ((size_t)bh * Nq + qrow) * D;
+    // Staging areas follow the exchange area (group 1 no longer reads LDS).
+    char* stage = reinterpret_cast<char*>(lds) + kMergeBytes + rw * OStage<D>::BYTES;
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const int d = db * 32 + i4 * 8 + hl * 4;
-          float v[4];
+      for (int i4 = 0; i4 < 4; ++i4) {
+        float v[4];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int i = i4 * 4 + j;
-            v[j] = o[db][i] * c0 + xo[((rw * DB + db) * 16 + i) * 64 + lane] * c1;
-          }
-          u32x2 w;
-          w[0] = pack_bf16x2(v[0], v[1]);
-          w[1] = pack_bf16x2(v[2], v[3]);
-          *reinterpret_cast<u32x2*>(orow + d) = w;
+        for (int j = 0; j < 4; ++j) {
+          const int i = i4 * 4 + j;
+          v[j] = o[db][i] * c0 + xo[((rw * DB + db) * 16 + i) * 64 + lane] * c1;
         }
-      if (lane < 32) LSE[(size_t)bh * Nq + qrow] = lsum > 0.f ? (M + fast_log2(lsum)) * kLn2 : kNegInf;
-    }
+        u32x2 w;
+        w[0] = pack_bf16x2(v[0], v[1]);
+        w[1] = pack_bf16x2(v[2], v[3]);
+        stage_o_cols<D>(stage, db, i4, w, lane);
+      }
+    store_o_staged<D>(stage, O + ((size_t)bh * Nq + qw0) * D, Nq - qw0, lane);
+    if (lane < 32 && qrow < Nq) LSE[(size_t)bh * Nq + qrow] = lsum > 0.f ? (M + fast_log2(lsum)) * kLn2 : kNegInf;
   }
   };
 
