@@ -396,18 +396,40 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(
     if (item + 1 < n_items) stage(buf ^ 1);
   }
 
-  // dK (times scale) and dV, bf16: lane holds d column, key rows kg*32 + (i/4)*8 + 4 hl + i%4.
+  // dK (times scale) and dV, bf16: lane holds d column (role DH + dt) 32 +
+  // l % 32 of key rows kg 32 + (r/4) 8 + 4 hl + r % 4. Stored straight from
+  // that layout, each instruction would write 2 bytes per lane; instead each
+  // wave stages its 32 keys x DH 32 columns of both in LDS (key-row-major,
+  // rows padded by 16 bytes) and stores 16 bytes per lane, whole row halves
+  // per instruction.
+  constexpr int SC = DH * 32;        // columns per wave
+  constexpr int SRS = SC * 2 + 16;   // staged row stride, bytes
+  constexpr int SB = 32 * SRS;       // one tensor's staged rows
+  static_assert(8 * 2 * SB <= (int)sizeof(lds), "dK/dV staging exceeds LDS");
+  __syncthreads();  // no wave reads the tiles or the exchange area any more
+  char* st = reinterpret_cast<char*>(lds) + wave * 2 * SB;
 #pragma unroll
-  for (int dt = 0; dt < DH; ++dt) {
-    const int d = (role * DH + dt) * 32 + (lane & 31);
+  for (int dt = 0; dt < DH; ++dt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int kl = kg * 32 + (r >> 2) * 8 + hl * 4 + (r & 3);
-      if (kl < nk) {
-        const size_t off = ((size_t)(b * Hkv + g) * Nk + k0 + kl) * D + d;
-        dK[off] = __builtin_bit_cast(uint16_t, (__bf16)(dk[dt][r] * scale));
-        dV[off] = __builtin_bit_cast(uint16_t, (__bf16)dv[dt][r]);
-      }
+      const int off = ((r >> 2) * 8 + hl * 4 + (r & 3)) * SRS + (dt * 32 + (lane & 31)) * 2;
+      *reinterpret_cast<uint16_t*>(st + off) = __builtin_bit_cast(uint16_t, (__bf16)(dk[dt][r] * scale));
+      *reinterpret_cast<uint16_t*>(st + SB + off) = __builtin_bit_cast(uint16_t, (__bf16)dv[dt][r]);
+    }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  constexpr int LPR = SC * 2 / 16;  // lanes per staged row
+  constexpr int RPS = 64 / LPR;     // rows per store instruction
+  const size_t row0 = (size_t)(b * Hkv + g) * Nk + k0 + kg * 32;
+#pragma unroll
+  for (int j = 0; j < 32 / RPS; ++j) {
+    const int r = j * RPS + lane / LPR;
+    const int c = (lane % LPR) * 16;
+    const u32x4 vk = *reinterpret_cast<const u32x4*>(st + r * SRS + c);
+    const u32x4 vv = *reinterpret_cast<const u32x4*>(st + SB + r * SRS + c);
+    if (kg * 32 + r < nk) {
+      const size_t off = (row0 + r) * D * 2 + role * SC * 2 + c;
+      *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(dK) + off) = vk;
+      *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(dV) + off) = vv;
     }
   }
 }
@@ -616,16 +638,34 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(
 
   // dQ (times scale), bf16. C layout of dQ^T: lane l holds row qw, d columns
   // (role DH + dt)*32 + 8 a + 4 hl + 0..3 (a = 0..3) in elements 4 a + 0..3.
-  if (qin) {
-    uint16_t* out = dQ + ((size_t)bh * Nq + qw) * D + role * DH * 32;
+  // Staged per wave in LDS (row-major, rows padded by 16 bytes) and stored 16
+  // bytes per lane, whole row halves per instruction, instead of 8 bytes into
+  // each of 32 rows.
+  constexpr int SC = DH * 32;       // columns per wave
+  constexpr int SRS = SC * 2 + 16;  // staged row stride, bytes
+  static_assert(8 * 32 * SRS <= (int)sizeof(lds), "dQ staging exceeds LDS");
+  __syncthreads();  // no wave reads the K/V tiles or the exchange area any more
+  char* st = reinterpret_cast<char*>(lds) + wave * 32 * SRS;
 #pragma unroll
-    for (int dt = 0; dt < DH; ++dt)
+  for (int dt = 0; dt < DH; ++dt)
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const u32x2 w = u32x2{pack_bf16x2(dq[dt][4 * a] * scale, dq[dt][4 * a + 1] * scale),
-                              pack_bf16x2(dq[dt][4 * a + 2] * scale, dq[dt][4 * a + 3] * scale)};
-        *reinterpret_cast<u32x2*>(out + dt * 32 + a * 8 + hl * 4) = w;
-      }
+    for (int a = 0; a < 4; ++a) {
+      const u32x2 w = u32x2{pack_bf16x2(dq[dt][4 * a] * scale, dq[dt][4 * a + 1] * scale),
+                            pack_bf16x2(dq[dt][4 * a + 2] * scale, dq[dt][4 * a + 3] * scale)};
+      *reinterpret_cast<u32x2*>(st + (lane & 31) * SRS + (dt * 32 + a * 8 + hl * 4) * 2) = w;
+    }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  constexpr int LPR = SC * 2 / 16;  // lanes per staged row
+  constexpr int RPS = 64 / LPR;     // rows per store instruction
+  const int qrow0 = q0 + rg * 32;
+#pragma unroll
+  for (int j = 0; j < 32 / RPS; ++j) {
+    const int r = j * RPS + lane / LPR;
+    const int c = (lane % LPR) * 16;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(st + r * SRS + c);
+    if (qrow0 + r < Nq)
+      *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(dQ) + ((size_t)bh * Nq + qrow0 + r) * D * 2 + role * SC * 2 +
+                                c) = v;
   }
 }
 

@@ -13,8 +13,9 @@
 // FA2 loop of the 5090 page's "Flash Attention 2 algorithm" pseudocode with
 // the online softmax of its "v1 -- basic version" bullets, 8 waves in two
 // KV-parity groups, two-phase ping-pong (one wave of a SIMD on MFMAs while
-// the other runs the softmax), direct global->LDS tile copies, a guarded
-// exponent reference, causal tile skipping, XCD-aware workgroup order.
+// the other runs the softmax), direct global->LDS tile copies, Q and O moved
+// through LDS by whole rows, a guarded exponent reference, causal tile
+// skipping, XCD-aware workgroup order.
 //
 // What changes for 8-bit inputs:
 //  * Both products use v_mfma_f32_32x32x64_f8f6f4 with E4M3 operands (twice
@@ -60,9 +61,13 @@ constexpr int kF8VBase = kF8Slots * kF8Tile;   // V slots follow the K slots
 constexpr int kF8Copies = 2;     // 1 KiB copy instructions per wave per tile (4 waves per group)
 constexpr float kF8Off = 4.f;    // log2 of the largest probability after a reference update
 constexpr float kF8SumHi = 448.f;
-// LDS: 64 KiB of tiles; the final merge reuses it for 66 KiB.
+// LDS: 64 KiB of tiles; the final merge reuses it for 66 KiB, followed by
+// group 0's O staging areas (4 x 32 rows of 256 + 16 bytes).
 constexpr int kF8MergeBytes = 4 * 4 * 16 * 64 * 4 + 2 * 4 * 64 * 4;
-constexpr int kF8Lds = kF8MergeBytes > 2 * kF8VBase ? kF8MergeBytes : 2 * kF8VBase;
+constexpr int kF8OStageRow = 2 * kF8D + 16;
+constexpr int kF8OStageBytes = 32 * kF8OStageRow;
+constexpr int kF8Lds = kF8MergeBytes + 4 * kF8OStageBytes > 2 * kF8VBase ? kF8MergeBytes + 4 * kF8OStageBytes
+                                                                         : 2 * kF8VBase;
 
 // 16-byte-chunk XOR swizzle of a 128-byte row. Two rows share the 64 banks
 // (odd rows on the upper 32), so the chunk is XORed with a bijection of row
@@ -131,17 +136,8 @@ __global__ __launch_bounds__(kF8Threads) void fwd_fp8_kernel(
   const int diag = Nk - Nq;
 
   // Q rows as B operands: half dh of d, lane-half hl holds bytes 64 dh + 32 hl .. +31.
+  // They are read from LDS below (see the prologue).
   i32x8 qf[2];
-#pragma unroll
-  for (int dh = 0; dh < 2; ++dh) {
-    if (qrow < Nq) {
-      const u32x4* src = reinterpret_cast<const u32x4*>(Qh + (size_t)qrow * D + dh * 64 + hl * 32);
-      const u32x4 lo = src[0], hi = src[1];
-      qf[dh] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-    } else {
-      qf[dh] = i32x8{};
-    }
-  }
 
   // Loop-invariant LDS byte offsets. K operand (key row lane % 32 of a 32-key
   // block, chunks 4 dh + 2 hl + c); the block and slot are immediates.
@@ -171,6 +167,18 @@ __global__ __launch_bounds__(kF8Threads) void fwd_fp8_kernel(
     goff[i] = (uint32_t)(row * D + swz8(row, lane & 7) * 16);
   }
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(lds));
+  // The wave's 32 Q rows are copied by whole rows into a wave-private area
+  // laid out as the first 32 rows of a K tile (K slots 2-3 for group 0, V
+  // slots 2-3 for group 1, which no copy fills before the loop's first
+  // barrier) and read back through the K operand offsets. Rows past Nq
+  // repeat row Nq - 1 (finite data whose results are not stored).
+  const uint32_t qstage = (grp == 0 ? 2 * kF8Tile : kF8VBase + 2 * kF8Tile) + rw * 32 * D;
+#pragma unroll
+  for (int i = 0; i < 32 * D / 1024; ++i) {
+    const int row = i * 8 + (lane >> 3);
+    const int grow = qw0 + row < Nq ? qw0 + row : Nq - 1;
+    dma16_sbase(Qh, (uint32_t)(grow * D + swz8(row, lane & 7) * 16), lds0 + qstage + i * 1024);
+  }
 
   int kv_end = Nk;
   if (causal) {
@@ -309,6 +317,12 @@ __global__ __launch_bounds__(kF8Threads) void fwd_fp8_kernel(
   }
   wait_vmcnt0();
 #pragma unroll
+  for (int dh = 0; dh < 2; ++dh) {
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(lds_c + qstage + koff[dh][0]);
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(lds_c + qstage + koff[dh][1]);
+    qf[dh] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+  }
+#pragma unroll
   for (int dh = 0; dh < 2; ++dh) asm volatile("" ::"v"(qf[dh]));
   __syncthreads();
 
@@ -397,26 +411,36 @@ __global__ __launch_bounds__(kF8Threads) void fwd_fp8_kernel(
     const float lsum = l_tot * a0 + l1 * a1;
     const float inv = lsum > 0.f ? vds / lsum : 0.f;
     const float c0 = a0 * inv, c1 = a1 * inv;
-    if (qrow < Nq) {
-      uint16_t* orow = O + ((size_t)bh * Nq + qrow) * D;
+    // O rows staged in a wave-private, 16-byte-padded LDS area after the
+    // exchange area and stored by whole rows (4 rows per instruction)
+    // instead of 8 bytes into each of 32 rows.
+    char* stage = reinterpret_cast<char*>(lds) + kF8MergeBytes + rw * kF8OStageBytes;
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
+    for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const int d = db * 32 + i4 * 8 + hl * 4;
-          float v[4];
+      for (int i4 = 0; i4 < 4; ++i4) {
+        float v[4];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int i = i4 * 4 + j;
-            v[j] = o[db][i] * c0 + xo[((rw * 4 + db) * 16 + i) * 64 + lane] * c1;
-          }
-          u32x2 w;
-          w[0] = pack_bf16x2(v[0], v[1]);
-          w[1] = pack_bf16x2(v[2], v[3]);
-          *reinterpret_cast<u32x2*>(orow + d) = w;
+        for (int j = 0; j < 4; ++j) {
+          const int i = i4 * 4 + j;
+          v[j] = o[db][i] * c0 + xo[((rw * 4 + db) * 16 + i) * 64 + lane] * c1;
         }
-      if (lane < 32) LSE[(size_t)bh * Nq + qrow] = lsum > 0.f ? (M + fast_log2(lsum)) * kLn2 : kNegInf;
+        u32x2 w;
+        w[0] = pack_bf16x2(v[0], v[1]);
+        w[1] = pack_bf16x2(v[2], v[3]);
+        *reinterpret_cast<u32x2*>(stage + (lane & 31) * kF8OStageRow + (db * 32 + i4 * 8 + hl * 4) * 2) = w;
+      }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    const int nvalid = Nq - qw0;
+    char* o_rows = reinterpret_cast<char*>(O + ((size_t)bh * Nq + qw0) * D);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int r = j * 4 + (lane >> 4);
+      const int c = (lane & 15) * 16;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(stage + r * kF8OStageRow + c);
+      if (r < nvalid) *reinterpret_cast<u32x4*>(o_rows + (size_t)r * 2 * D + c) = v;
     }
+    if (lane < 32 && qrow < Nq) LSE[(size_t)bh * Nq + qrow] = lsum > 0.f ? (M + fast_log2(lsum)) * kLn2 : kNegInf;
   }
 }
 
