@@ -103,35 +103,38 @@ __device__ __forceinline__ bf16x8 row_operand(const uint16_t* tile, int r0, int 
   return *reinterpret_cast<const bf16x8*>(tile + (r0 + (lane & 31)) * RS + k0 + (lane >> 5) * 8);
 }
 
-// Copy of 64 rows of a [rows][D] bf16 tensor into a padded LDS tile (missing
-// rows zero) in two halves: global loads into registers (issued one block
-// ahead, so that their latency hides under the current block's work), then
-// the stores into the tile.
-template <int D>
+// Copy of 64 rows of a [rows][D] bf16 tensor into a padded LDS tile in two
+// halves: global loads into registers (issued one block ahead, so that their
+// latency hides under the current block's work), then the stores into the
+// tile. Rows past `nrows` repeat row nrows - 1: finite data whose products
+// the kernels zero (keys past Nk are masked, rows past Nq have P = 0 through
+// their LSE); a tile with no valid row is zero and issues no load. Every
+// load is unconditional: a select between a load and zero makes the
+// compiler zero the destination first, and it then waits for all loads in
+// flight before each such write, which serialises the block's loads.
+template <int D, int NT = kBwdThreads>
 struct RowsInFlight {
   static constexpr int CH = D / 8;
-  static constexpr int N = 64 * CH / kBwdThreads;
+  static constexpr int N = 64 * CH / NT;
   u32x4 r[N];
   __device__ __forceinline__ void load(const uint16_t* __restrict__ src, int nrows, int tid) {
-    if (nrows == 64) {
+    if (nrows <= 0) {
 #pragma unroll
-      for (int i = 0; i < N; ++i) {
-        const int id = tid + i * kBwdThreads;
-        r[i] = *reinterpret_cast<const u32x4*>(src + (size_t)(id / CH) * D + (id % CH) * 8);
-      }
+      for (int i = 0; i < N; ++i) r[i] = u32x4{0u, 0u, 0u, 0u};
       return;
     }
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-      const int id = tid + i * kBwdThreads;
+      const int id = tid + i * NT;
       const int row = id / CH, ch = id % CH;
-      r[i] = row < nrows ? *reinterpret_cast<const u32x4*>(src + (size_t)row * D + ch * 8) : u32x4{0u, 0u, 0u, 0u};
+      const int rr = row < nrows ? row : nrows - 1;
+      r[i] = *reinterpret_cast<const u32x4*>(src + (size_t)rr * D + ch * 8);
     }
   }
   __device__ __forceinline__ void store(uint16_t* tile, int tid) const {
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-      const int id = tid + i * kBwdThreads;
+      const int id = tid + i * NT;
       *reinterpret_cast<u32x4*>(tile + (id / CH) * BwdLayout<D>::RS + (id % CH) * 8) = r[i];
     }
   }
@@ -240,7 +243,11 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(
   // Work items: (query head of the group, query block), query block fastest.
   const int per_head = n_qb > qb0 ? n_qb - qb0 : 0;
   const int n_items = group * per_head;
-  RowsInFlight<D> qn, don;
+  // The next block's Q and dO rows are loaded and staged by the role-0 waves
+  // alone (threads 0..255), which wait at the swap barrier for their slower
+  // partners anyway: their loads issue there instead of on every wave's
+  // critical path.
+  RowsInFlight<D, kBwdThreads / 2> qn, don;
   float lse_n = kNegInf, d_n = 0.f;
   auto fetch = [&](int item) __attribute__((always_inline)) {
     const int hh = item / per_head, qb = qb0 + item % per_head;
@@ -263,7 +270,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(
       rowv[buf * 128 + 64 + tid] = d_n;
     }
   };
-  if (n_items > 0) {
+  if (n_items > 0 && role == 0) {
     fetch(0);
     stage(0);
   }
@@ -280,7 +287,6 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(
     // This block's rows are in LDS, and every wave is done with the other
     // buffer (the previous block), which the next block now goes into.
     __syncthreads();
-    if (item + 1 < n_items) fetch(item + 1);
 
     // Masks are needed only at a ragged key block or where the causal
     // diagonal crosses the block (row 0 of the block sees its last key
@@ -379,6 +385,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(
       tiles(std::false_type{});
     else
       tiles(std::true_type{});
+    if (role == 0 && item + 1 < n_items) fetch(item + 1);
     __syncthreads();  // both halves of every key group's P and dS are in LDS
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
@@ -393,7 +400,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(
       dvdk(qt, pa, da);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (item + 1 < n_items) stage(buf ^ 1);
+    if (role == 0 && item + 1 < n_items) stage(buf ^ 1);
   }
 
   // dK (times scale) and dV, bf16: lane holds d column (role DH + dt) 32 +
