@@ -284,23 +284,47 @@ def _visible_keys(w, rows):
     return np.clip(rows + 1 + (w.Nk - w.Nq), 0, w.Nk)
 
 
-def cpu_baseline(w, budget_s=15.0, row_block=1024):
+def cpu_baseline(w, budget_s=15.0, row_block=1024, kind="attention"):
     """The fp64 oracle on the host over a bounded sample of the workload: (batch,
     head) slabs in order, each in blocks of query rows, until the budget is
     spent. Prefill reports TFLOP/s (the FLOPs of the rows done); decode reports
-    GB/s (the algorithmic bytes of the slabs done, as for the GPU line)."""
+    GB/s (the algorithmic bytes of the slabs done, as for the GPU line).
+    `kind` picks the oracle: "attention" (bf16 inputs), "fp8" (E4M3 inputs,
+    decoded inside the timed call), "backward" (the gradients of a row block
+    against all of its head's keys: dQ of those rows and their share of dK
+    and dV; credited 2.5x the forward FLOPs, as the GPU line) or "paged"
+    (one sequence at a time, its keys gathered from a page cache in a random
+    page order)."""
     import oracle
+    if kind == "paged":
+        return _cpu_baseline_paged(w, budget_s)
     group = w.Hq // w.Hkv
     t_total, flops, rows_done, slabs = 0.0, 0.0, 0, 0
     for b in range(w.B):
         for h in range(w.Hq):
             for r0 in range(0, w.Nq, row_block):
                 rows = np.arange(r0, min(w.Nq, r0 + row_block))
-                q, k, v = synth.inputs_f64(w, q_heads=[(b, h)], kv_heads=[(b, h // group)], q_rows=rows)
-                t0 = time.perf_counter()
-                oracle.attention(q[:, None], k[:, None], v[:, None], w.scale, w.causal, q_index=rows, nq=w.Nq)
+                if kind == "fp8":
+                    q8 = synth.draw_e4m3(w.seed, synth.TENSOR_Q, w.q_shape, heads=[(b, h)], rows=rows)
+                    k8 = synth.draw_e4m3(w.seed, synth.TENSOR_K, w.kv_shape, heads=[(b, h // group)])
+                    v8 = synth.draw_e4m3(w.seed, synth.TENSOR_V, w.kv_shape, heads=[(b, h // group)])
+                    t0 = time.perf_counter()
+                    oracle.attention_fp8(q8[:, None], k8[:, None], v8[:, None], synth.FP8_DESCALE, w.scale,
+                                         w.causal, q_index=rows, nq=w.Nq)
+                elif kind == "backward":
+                    q, k, v = synth.inputs_f64(w, q_heads=[(b, h)], kv_heads=[(b, h // group)], q_rows=rows)
+                    do = synth.bf16_bits_to_f32(synth.draw_bf16(w.seed, synth.TENSOR_DO, w.q_shape,
+                                                                heads=[(b, h)], rows=rows)).astype(np.float64)
+                    if w.causal:
+                        raise ValueError("the backward baseline samples row blocks of non-causal workloads")
+                    t0 = time.perf_counter()
+                    oracle.attention_backward_head(q[0], k[0], v[0], do[0], w.scale, False)
+                else:
+                    q, k, v = synth.inputs_f64(w, q_heads=[(b, h)], kv_heads=[(b, h // group)], q_rows=rows)
+                    t0 = time.perf_counter()
+                    oracle.attention(q[:, None], k[:, None], v[:, None], w.scale, w.causal, q_index=rows, nq=w.Nq)
                 t_total += time.perf_counter() - t0
-                flops += 4.0 * w.d * float(_visible_keys(w, rows).sum())
+                flops += (2.5 if kind == "backward" else 1.0) * 4.0 * w.d * float(_visible_keys(w, rows).sum())
                 rows_done += len(rows)
                 if t_total >= budget_s:
                     break
@@ -311,14 +335,47 @@ def cpu_baseline(w, budget_s=15.0, row_block=1024):
             break
     out = host_info()
     frac = rows_done / max(w.B * w.Hq * w.Nq, 1)
+    what = {"attention": "fp64 numpy", "fp8": "E4M3 decode + fp64 numpy",
+            "backward": "fp64 numpy gradients"}[kind]
     sample = (f"{rows_done} of {w.B * w.Hq * w.Nq} query rows ({slabs} (batch, head) slabs) of {w.name}, "
-              f"{t_total:.1f} s of fp64 numpy on the host")
+              f"{t_total:.1f} s of {what} on the host")
     if w.num_splits:
         return {"value": w.algorithmic_bytes() * frac / t_total / 1e9, "unit": "GB/s",
                 "cores": out["cores"], "kind": "oracle", "sample": sample,
                 "cpu_model": out["cpu_model"], "blas": out["blas"]}
     return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": out["cores"], "kind": "oracle",
             "sample": sample, "cpu_model": out["cpu_model"], "blas": out["blas"]}
+
+
+def _cpu_baseline_paged(w, budget_s, page=PAGE):
+    """cpu_baseline for the paged decode: per sequence, its K/V pages stored in
+    a random page order, then the oracle's gather and attention (timed)."""
+    import oracle
+    t_total, seqs = 0.0, 0
+    n_pages = -(-w.Nk // page)
+    for b in range(w.B):
+        q, k, v = synth.inputs_f64(w, q_heads=[(b, h) for h in range(w.Hq)],
+                                   kv_heads=[(b, h) for h in range(w.Hkv)])
+        _, table = synth.page_table(1, n_pages, w.seed + b)
+        pad = n_pages * page - w.Nk
+        kp = np.pad(k, ((0, 0), (0, pad), (0, 0))).reshape(w.Hkv, n_pages, page, w.d).transpose(1, 0, 2, 3)
+        vp = np.pad(v, ((0, 0), (0, pad), (0, 0))).reshape(w.Hkv, n_pages, page, w.d).transpose(1, 0, 2, 3)
+        k_cache = np.empty_like(kp)
+        v_cache = np.empty_like(vp)
+        k_cache[table[0]] = kp
+        v_cache[table[0]] = vp
+        t0 = time.perf_counter()
+        oracle.paged_attention(q[None], k_cache, v_cache, table, np.array([w.Nk]), w.scale, w.causal)
+        t_total += time.perf_counter() - t0
+        seqs += 1
+        if t_total >= budget_s:
+            break
+    out = host_info()
+    nbytes = (w.algorithmic_bytes() + w.B * n_pages * 4 + w.B * 4) * seqs / w.B
+    return {"value": nbytes / t_total / 1e9, "unit": "GB/s", "cores": out["cores"], "kind": "oracle",
+            "sample": f"{seqs} of {w.B} sequences of {w.name}_paged{page} ({page}-key pages in a random order), "
+                      f"{t_total:.1f} s of fp64 numpy on the host",
+            "cpu_model": out["cpu_model"], "blas": out["blas"]}
 
 
 def rocm_version():
@@ -598,6 +655,11 @@ def main():
             log(f"  {name}: {others[name]['cpu_baseline']}")
         line["decode"]["cpu_baseline"] = cpu_baseline(wd, budget_s=3.0)
         log(f"  decode: {line['decode']['cpu_baseline']}")
+        for key, wl, kind in (("prefill_fp8", w8, "fp8"), ("prefill_d256", w256, "attention"),
+                              ("prefill_d192", w192, "attention"), ("backward", wp, "backward"),
+                              ("decode_paged", wd, "paged")):
+            line[key]["cpu_baseline"] = cpu_baseline(wl, budget_s=2.0, kind=kind)
+            log(f"  {key}: {line[key]['cpu_baseline']}")
     print(json.dumps(line), flush=True)
 
 
