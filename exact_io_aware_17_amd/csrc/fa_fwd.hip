@@ -543,8 +543,11 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_bf16_kernel(
   wait_vmcnt0();
   __syncthreads();
 
-  // Merge the two groups (same rows, disjoint key sets) and write out.
-  float* xo = reinterpret_cast<float*>(lds);                     // [4 rw][DB][16][64] fp32
+  // Merge the two groups (same rows, disjoint key sets) and write out. The
+  // O exchange holds each lane's accumulator registers 4 at a time, so that
+  // every LDS access moves 16 bytes per lane (conflict-free: consecutive
+  // lanes, consecutive 16-byte chunks).
+  f32x4* xo = reinterpret_cast<f32x4*>(lds);                     // [4 rw][DB][4 i4][64] fp32 x4
   float* xm = reinterpret_cast<float*>(lds) + 4 * DB * 16 * 64;  // [4 rw][64] m, then [4 rw][64] l
   constexpr int kMergeBytes = (4 * DB * 16 * 64 + 2 * 4 * 64) * 4;
   static_assert(kMergeBytes + 4 * OStage<D>::BYTES <= (int)sizeof(lds), "merge and staging exceed LDS");
@@ -554,7 +557,9 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_bf16_kernel(
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) xo[((rw * DB + db) * 16 + i) * 64 + lane] = o[db][i];
+      for (int i4 = 0; i4 < 4; ++i4)
+        xo[((rw * DB + db) * 4 + i4) * 64 + lane] =
+            f32x4{o[db][4 * i4], o[db][4 * i4 + 1], o[db][4 * i4 + 2], o[db][4 * i4 + 3]};
     xm[rw * 64 + lane] = m_run;
     xm[256 + rw * 64 + lane] = l_tot;
   }
@@ -574,12 +579,10 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_bf16_kernel(
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
+        const f32x4 x = xo[((rw * DB + db) * 4 + i4) * 64 + lane];
         float v[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int i = i4 * 4 + j;
-          v[j] = o[db][i] * c0 + xo[((rw * DB + db) * 16 + i) * 64 + lane] * c1;
-        }
+        for (int j = 0; j < 4; ++j) v[j] = o[db][i4 * 4 + j] * c0 + x[j] * c1;
         u32x2 w;
         w[0] = pack_bf16x2(v[0], v[1]);
         w[1] = pack_bf16x2(v[2], v[3]);

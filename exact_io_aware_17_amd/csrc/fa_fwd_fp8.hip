@@ -390,14 +390,18 @@ __global__ __launch_bounds__(kF8Threads) void fwd_fp8_kernel(
 
   // Merge the two groups and write out (O^T accumulator: lane l, register i
   // of block db holds d = 32 db + (i/4)*8 + 4 hl + i%4 of query row qrow).
-  float* xo = reinterpret_cast<float*>(lds);
+  // O exchange: each lane's accumulator registers 4 at a time (16-byte,
+  // conflict-free LDS accesses).
+  f32x4* xo = reinterpret_cast<f32x4*>(lds);  // [4 rw][4 db][4 i4][64] fp32 x4
   float* xm = reinterpret_cast<float*>(lds) + 4 * 4 * 16 * 64;
   const float l_tot = l_run;
   if (grp == 1) {
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) xo[((rw * 4 + db) * 16 + i) * 64 + lane] = o[db][i];
+      for (int i4 = 0; i4 < 4; ++i4)
+        xo[((rw * 4 + db) * 4 + i4) * 64 + lane] =
+            f32x4{o[db][4 * i4], o[db][4 * i4 + 1], o[db][4 * i4 + 2], o[db][4 * i4 + 3]};
     xm[rw * 64 + lane] = m_run;
     xm[256 + rw * 64 + lane] = l_tot;
   }
@@ -419,12 +423,10 @@ __global__ __launch_bounds__(kF8Threads) void fwd_fp8_kernel(
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
+        const f32x4 x = xo[((rw * 4 + db) * 4 + i4) * 64 + lane];
         float v[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int i = i4 * 4 + j;
-          v[j] = o[db][i] * c0 + xo[((rw * 4 + db) * 16 + i) * 64 + lane] * c1;
-        }
+        for (int j = 0; j < 4; ++j) v[j] = o[db][i4 * 4 + j] * c0 + x[j] * c1;
         u32x2 w;
         w[0] = pack_bf16x2(v[0], v[1]);
         w[1] = pack_bf16x2(v[2], v[3]);

@@ -53,7 +53,15 @@ struct WideLayout {
   static constexpr int kThreads = 64 * k2WavesPerGroup * NG;
   static constexpr int kVBase = 2 * NG * kTile;  // two K slots per group, then two V slots per group
   static constexpr int kMergeBytes = NG == 2 ? 4 * (D / 32) * 16 * 64 * 4 + 2048 : 0;
-  static constexpr int kLds = kMergeBytes > 2 * kVBase ? kMergeBytes : 2 * kVBase + (NG == 2 ? 2048 : 0);
+  // O staging (per wave, 32 rows x 64 columns at a time, rows padded by 16
+  // bytes): after the exchange area with two groups, at the start of LDS with
+  // one (the tile slots are free by then).
+  static constexpr int kStageRow = 64 * 2 + 16;
+  static constexpr int kStageBytes = 32 * kStageRow;
+  static constexpr int kStageBase = kMergeBytes;
+  static constexpr int kLdsTiles = 2 * kVBase + (NG == 2 ? 2048 : 0);
+  static constexpr int kLdsMerge = kMergeBytes + (NG == 2 ? 4 : 4) * kStageBytes;
+  static constexpr int kLds = kLdsMerge > kLdsTiles ? kLdsMerge : kLdsTiles;
   // Lane offsets kept per wave: at d = 256 copy instructions i and i + 2
   // cover rows 16 apart with the same swizzle, so two offsets serve all four
   // (the other two through a scalar base 16 rows further on).
@@ -304,37 +312,60 @@ __global__ __launch_bounds__(64 * k2WavesPerGroup * NG, 2 / NG) void fwd_bf16_wi
     step(u + 1, std::integral_constant<int, 1>{});
   }
 
-  // Merge the two groups (same rows, disjoint key sets) and write out.
-  float* xo = reinterpret_cast<float*>(lds);                        // [4 rw][DB][16][64] fp32
+  // Merge the two groups (same rows, disjoint key sets) and write out. The
+  // O exchange holds each lane's accumulator registers 4 at a time (16-byte,
+  // conflict-free LDS accesses). O rows are stored through a wave-private
+  // LDS staging area, 64 columns at a time: written in accumulator order,
+  // read back row-major, so that each 16-byte-per-lane store covers 8 whole
+  // 128-byte row pieces instead of 8 bytes of each of 32 rows.
+  f32x4* xo = reinterpret_cast<f32x4*>(lds);                        // [4 rw][DB][4 i4][64] fp32 x4
   float* xm = reinterpret_cast<float*>(lds) + 4 * DB * 16 * 64;     // [4 rw][64] m, then [4 rw][64] l
-  if (NG == 1) {
-    if (qrow < Nq) {
-      const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-      uint16_t* orow = O + ((size_t)bh * Nq + qrow) * D;
+  char* stage = reinterpret_cast<char*>(lds) + L::kStageBase + rw * L::kStageBytes;
+  char* o_rows = reinterpret_cast<char*>(O + ((size_t)bh * Nq + qw0) * D);
+  const int nvalid = Nq - qw0;
+  // Columns 64 c .. 64 c + 63 (d blocks 2 c, 2 c + 1) of this wave's rows:
+  // `val(db, i)` gives the final value of accumulator register i of block db.
+  auto store_chunk = [&](int c, auto val) __attribute__((always_inline)) {
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+    for (int k = 0; k < 2; ++k)
 #pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const int d = db * 32 + i4 * 8 + hl * 4;
-          u32x2 w;
-          w[0] = pack_bf16x2(o[db][i4 * 4] * inv, o[db][i4 * 4 + 1] * inv);
-          w[1] = pack_bf16x2(o[db][i4 * 4 + 2] * inv, o[db][i4 * 4 + 3] * inv);
-          *reinterpret_cast<u32x2*>(orow + d) = w;
-        }
-      if (lane < 32) LSE[(size_t)bh * Nq + qrow] = l_run > 0.f ? (m_run + fast_log2(l_run)) * kLn2 : kNegInf;
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int db = 2 * c + k;
+        u32x2 w;
+        w[0] = pack_bf16x2(val(db, i4 * 4), val(db, i4 * 4 + 1));
+        w[1] = pack_bf16x2(val(db, i4 * 4 + 2), val(db, i4 * 4 + 3));
+        *reinterpret_cast<u32x2*>(stage + (lane & 31) * L::kStageRow + (k * 32 + i4 * 8 + hl * 4) * 2) = w;
+      }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = j * 8 + (lane >> 3);
+      const int cb = (lane & 7) * 16;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(stage + r * L::kStageRow + cb);
+      if (r < nvalid) *reinterpret_cast<u32x4*>(o_rows + (size_t)r * 2 * D + c * 128 + cb) = v;
     }
+  };
+  if (NG == 1) {
+    // One group: each wave holds whole rows. The loop's last barrier has
+    // passed, so the tile slots are free for staging.
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+#pragma unroll
+    for (int c = 0; c < DB / 2; ++c) store_chunk(c, [&](int db, int i) { return o[db][i] * inv; });
+    if (lane < 32 && qrow < Nq) LSE[(size_t)bh * Nq + qrow] = l_run > 0.f ? (m_run + fast_log2(l_run)) * kLn2 : kNegInf;
     return;
   }
   if (grp == 1) {
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) xo[((rw * DB + db) * 16 + i) * 64 + lane] = o[db][i];
+      for (int i4 = 0; i4 < 4; ++i4)
+        xo[((rw * DB + db) * 4 + i4) * 64 + lane] =
+            f32x4{o[db][4 * i4], o[db][4 * i4 + 1], o[db][4 * i4 + 2], o[db][4 * i4 + 3]};
     xm[rw * 64 + lane] = m_run;
     xm[256 + rw * 64 + lane] = l_run;
   }
   __syncthreads();
-  if (grp == 0 && qrow < Nq) {
+  if (grp == 0) {
     const float m1 = xm[rw * 64 + lane];
     const float l1 = xm[256 + rw * 64 + lane];
     const float M = fmaxf(m_run, m1);
@@ -343,24 +374,16 @@ __global__ __launch_bounds__(64 * k2WavesPerGroup * NG, 2 / NG) void fwd_bf16_wi
     const float lsum = l_run * a0 + l1 * a1;
     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
     const float c0 = a0 * inv, c1 = a1 * inv;
-    uint16_t* orow = O + ((size_t)bh * Nq + qrow) * D;
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int c = 0; c < DB / 2; ++c) {
+      f32x4 x[2][4];
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const int d = db * 32 + i4 * 8 + hl * 4;
-        float v[4];
+      for (int k = 0; k < 2; ++k)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int i = i4 * 4 + j;
-          v[j] = o[db][i] * c0 + xo[((rw * DB + db) * 16 + i) * 64 + lane] * c1;
-        }
-        u32x2 w;
-        w[0] = pack_bf16x2(v[0], v[1]);
-        w[1] = pack_bf16x2(v[2], v[3]);
-        *reinterpret_cast<u32x2*>(orow + d) = w;
-      }
-    if (lane < 32) LSE[(size_t)bh * Nq + qrow] = lsum > 0.f ? (M + fast_log2(lsum)) * kLn2 : kNegInf;
+        for (int i4 = 0; i4 < 4; ++i4) x[k][i4] = xo[((rw * DB + 2 * c + k) * 4 + i4) * 64 + lane];
+      store_chunk(c, [&](int db, int i) { return o[db][i] * c0 + x[db - 2 * c][i >> 2][i & 3] * c1; });
+    }
+    if (lane < 32 && qrow < Nq) LSE[(size_t)bh * Nq + qrow] = lsum > 0.f ? (M + fast_log2(lsum)) * kLn2 : kNegInf;
   }
 }
 
