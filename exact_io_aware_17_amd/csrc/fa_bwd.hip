@@ -16,8 +16,9 @@
 //    dP = dO V^T). The workgroup walks the query heads of its GQA group and
 //    their 64-row query blocks (under the causal mask only the blocks that
 //    see a key of the block), Q, dO, LSE and D double-buffered in LDS (the
-//    next block's rows are loaded into registers while the current one is
-//    computed). Per query block:
+//    next block's rows are loaded into registers by the four waves that
+//    would otherwise wait at the block's exchange barrier, and stored into
+//    LDS after the block's products). Per query block:
 //      - wave w + 4 r computes, for the 32-row half r of the block, S and dP
 //        (32 rows x the pair's 32 keys) with 32x32x16 bf16 MFMAs;
 //        P = exp2(S scale log2e - LSE log2e), dS = P (dP - D) in fp32,
