@@ -436,8 +436,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(
     const u32x4 vv = *reinterpret_cast<const u32x4*>(st + SB + r * SRS + c);
     if (kg * 32 + r < nk) {
       const size_t off = (row0 + r) * D * 2 + role * SC * 2 + c;
-      *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(dK) + off) = vk;
-      *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(dV) + off) = vv;
+      __builtin_nontemporal_store(vk, reinterpret_cast<u32x4*>(reinterpret_cast<char*>(dK) + off));
+      __builtin_nontemporal_store(vv, reinterpret_cast<u32x4*>(reinterpret_cast<char*>(dV) + off));
     }
   }
 }
@@ -672,8 +672,9 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(
     const int c = (lane % LPR) * 16;
     const u32x4 v = *reinterpret_cast<const u32x4*>(st + r * SRS + c);
     if (qrow0 + r < Nq)
-      *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(dQ) + ((size_t)bh * Nq + qrow0 + r) * D * 2 + role * SC * 2 +
-                                c) = v;
+      __builtin_nontemporal_store(
+          v, reinterpret_cast<u32x4*>(reinterpret_cast<char*>(dQ) + ((size_t)bh * Nq + qrow0 + r) * D * 2 +
+                                      role * SC * 2 + c));
   }
 }
 

@@ -129,6 +129,13 @@ __device__ __forceinline__ void dma16_sbase(const void* sbase, uint32_t voff, ui
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds_base)
                : "memory", "m0");
 }
+// The same copy with the non-temporal hint, for rows read exactly once (the
+// query rows of a block).
+__device__ __forceinline__ void dma16_sbase_nt(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  lds_poison16(lds_base);
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(voff), "s"(sbase), "s"(lds_base)
+               : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
 __device__ __forceinline__ void wait_vmcnt0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }

@@ -141,8 +141,10 @@ __device__ __forceinline__ void stage_o_cols(char* stage, int db, int i4, u32x2 
   *reinterpret_cast<u32x2*>(stage + (lane & 31) * OStage<D>::RS + (db * 32 + i4 * 8 + (lane >> 5) * 4) * 2) = w;
 }
 
-// The staged rows to global memory, whole rows per instruction; rows at or
-// past `nvalid` are not written.
+// The staged rows to global memory, whole rows per instruction (with the
+// non-temporal hint: O is written once and not read here, so it need not
+// displace the K/V tiles the other workgroups still stream through L2); rows
+// at or past `nvalid` are not written.
 template <int D>
 __device__ __forceinline__ void store_o_staged(const char* stage, uint16_t* o_row0, int nvalid, int lane) {
   using S = OStage<D>;
@@ -152,7 +154,7 @@ __device__ __forceinline__ void store_o_staged(const char* stage, uint16_t* o_ro
     const int r = j * S::RPS + lane / S::LPR;
     const int c = (lane % S::LPR) * 16;
     const u32x4 v = *reinterpret_cast<const u32x4*>(stage + r * S::RS + c);
-    if (r < nvalid) *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(o_row0) + (size_t)r * 2 * D + c) = v;
+    if (r < nvalid) __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(reinterpret_cast<char*>(o_row0) + (size_t)r * 2 * D + c));
   }
 }
 
@@ -241,7 +243,7 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_bf16_kernel(
       const int row = i * L::ROWS_PER_KB + lane / L::CH;
       const int qr = qw0 + kappa(row);
       const int grow = qr < Nq ? qr : Nq - 1;
-      dma16_sbase(Qh, (uint32_t)(grow * D + swz<D>(row, lane % L::CH) * 8) * 2u, lds0 + qstage + i * 1024);
+      dma16_sbase_nt(Qh, (uint32_t)(grow * D + swz<D>(row, lane % L::CH) * 8) * 2u, lds0 + qstage + i * 1024);
     }
   } else {
 #pragma unroll

@@ -177,7 +177,7 @@ __global__ __launch_bounds__(kF8Threads) void fwd_fp8_kernel(
   for (int i = 0; i < 32 * D / 1024; ++i) {
     const int row = i * 8 + (lane >> 3);
     const int grow = qw0 + row < Nq ? qw0 + row : Nq - 1;
-    dma16_sbase(Qh, (uint32_t)(grow * D + swz8(row, lane & 7) * 16), lds0 + qstage + i * 1024);
+    dma16_sbase_nt(Qh, (uint32_t)(grow * D + swz8(row, lane & 7) * 16), lds0 + qstage + i * 1024);
   }
 
   int kv_end = Nk;
@@ -440,7 +440,7 @@ __global__ __launch_bounds__(kF8Threads) void fwd_fp8_kernel(
       const int r = j * 4 + (lane >> 4);
       const int c = (lane & 15) * 16;
       const u32x4 v = *reinterpret_cast<const u32x4*>(stage + r * kF8OStageRow + c);
-      if (r < nvalid) *reinterpret_cast<u32x4*>(o_rows + (size_t)r * 2 * D + c) = v;
+      if (r < nvalid) __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(o_rows + (size_t)r * 2 * D + c));
     }
     if (lane < 32 && qrow < Nq) LSE[(size_t)bh * Nq + qrow] = lsum > 0.f ? (M + fast_log2(lsum)) * kLn2 : kNegInf;
   }

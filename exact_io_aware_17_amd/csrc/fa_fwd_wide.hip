@@ -342,7 +342,7 @@ __global__ __launch_bounds__(64 * k2WavesPerGroup * NG, 2 / NG) void fwd_bf16_wi
       const int r = j * 8 + (lane >> 3);
       const int cb = (lane & 7) * 16;
       const u32x4 v = *reinterpret_cast<const u32x4*>(stage + r * L::kStageRow + cb);
-      if (r < nvalid) *reinterpret_cast<u32x4*>(o_rows + (size_t)r * 2 * D + c * 128 + cb) = v;
+      if (r < nvalid) __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(o_rows + (size_t)r * 2 * D + c * 128 + cb));
     }
   };
   if (NG == 1) {
