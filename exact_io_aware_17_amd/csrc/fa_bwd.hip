@@ -30,7 +30,9 @@
 //        LDS, and each wave accumulates dK and dV over all 64 rows for its
 //        half of d (32 keys x d/2 in registers), so that a wave fits in half
 //        of the SIMD's registers and one wave's softmax runs under the
-//        other's MFMAs.
+//        other's MFMAs. A wave runs the products of its own 32 rows from
+//        registers before the swap barrier and reads only its partner's
+//        operands after it.
 //  * bwd_dq_kernel: one workgroup (8 waves, two per SIMD) per (batch, query
 //    head, 128-row block). Waves w and w + 4 share 32 rows, whose Q and dO
 //    stay in registers. S and dP are recomputed transposed, S^T = K Q^T and
@@ -370,9 +372,9 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(
       }
     };
     // One straight-line body per case: this wave's tile, then the swap.
+    u32x4 pa[2], da[2];  // this wave's tile, [16-row step]
     auto tiles = [&](auto masked) __attribute__((always_inline)) {
       f32x16 s, dp;
-      u32x4 pa[2], da[2];  // [16-row step]
       sdp(role, s, dp);
       __builtin_amdgcn_sched_barrier(0);
       p_ds(masked, role, s, dp, pa, da);
@@ -387,18 +389,22 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(
     else
       tiles(std::true_type{});
     if (role == 0 && item + 1 < n_items) fetch(item + 1);
-    __syncthreads();  // both halves of every key group's P and dS are in LDS
-#pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-      // Tile qt's P and dS: written by wave kg + 4 qt.
+    // This wave's own tile needs no exchange: its dV/dK products run before
+    // the barrier, under the partner's softmax.
+    dvdk(role, pa, da);
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();  // the partner's P and dS are in LDS
+    {
+      // The partner's tile: written by wave kg + 4 (1 - role).
+      const int qt = role ^ 1;
       const u32x4* src = xch + (kg + 4 * qt) * 64 * 4;
-      u32x4 pa[2], da[2];
+      u32x4 pb[2], db[2];
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
-        pa[h2] = src[h2 * 64 + lane];
-        da[h2] = src[128 + h2 * 64 + lane];
+        pb[h2] = src[h2 * 64 + lane];
+        db[h2] = src[128 + h2 * 64 + lane];
       }
-      dvdk(qt, pa, da);
+      dvdk(qt, pb, db);
       __builtin_amdgcn_sched_barrier(0);
     }
     if (role == 0 && item + 1 < n_items) stage(buf ^ 1);
