@@ -323,13 +323,24 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_bf16_kernel(
       // per-lane bound, then a compare with a constant per score.
       const int L = causal && qrow + diag < Nk - 1 ? qrow + diag : Nk - 1;
       const int t = L - kv0 - 8 * hl;
+      // Each 32-key block is classified for the whole wave first (keys
+      // 32 mb + 0..23 in this lane's registers): on the causal diagonal one
+      // of the two is usually all visible or all masked, and only a mixed
+      // block needs the compare per score.
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+      for (int mb = 0; mb < 2; ++mb) {
+        if (__all(mb * 32 + 23 <= t)) continue;
+        if (__all(mb * 32 > t)) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) sc[mb][i] = kNegInf;
+          continue;
+        }
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int c = score_key(mb * 32, i, 0);
           if (c > t) sc[mb][i] = kNegInf;
         }
+      }
     }
     // Probabilities against the current reference; returns the tile's row sum.
     auto exps = [&]() __attribute__((always_inline)) {
