@@ -3,13 +3,16 @@ in which every tile copy first fills the LDS bytes it will write with NaN
 (all-ones: NaN in bf16, fp32 and E4M3). A read that runs ahead of a copy's
 wait and barrier, or lags behind the next copy into its slot, then reads NaN,
 which propagates into O; parity against the oracle on ragged, causal, GQA,
-head size 64/128/256, fp8 and full-size launches shows that no read does."""
+head size 64/128/192/256, every layout of the d = 64/128 kernel, fp8 and
+full-size launches shows that no read does."""
 import numpy as np
 import pytest
 
 import oracle
 import synth
 from gpu_helpers import assert_close, device_inputs, errors, oracle_full, oracle_sample, sample_rows, say
+import test_parity_fp8_gpu as fp8_tests
+from test_parity_gpu import ROW_GROUPS
 
 pytestmark = pytest.mark.gpu
 
@@ -54,6 +57,23 @@ def test_poison_bf16_full_oracle(fa_poison, w):
     o, lse = _run(fa_poison, w)
     o_ref, lse_ref = oracle_full(w)
     assert_close(errors(o, o_ref, lse, lse_ref), what=w.name + " (poison build)")
+
+
+@pytest.mark.parametrize("w", ROW_GROUPS, ids=lambda w: w.name)
+def test_poison_bf16_row_groups(fa_poison, w):
+    """The row-group layouts (both wave groups on their own rows, single
+    blocks and causal pairs) at sizes the oracle covers whole."""
+    assert fa_poison.fa_fwd_layout(w.B, w.Hq, w.Nq, w.d, w.causal).startswith("rows")
+    o, lse = _run(fa_poison, w)
+    o_ref, lse_ref = oracle_full(w)
+    assert_close(errors(o, o_ref, lse, lse_ref), what=w.name + " (poison build)")
+
+
+@pytest.mark.parametrize("w", fp8_tests.SMALL, ids=lambda w: w.name)
+def test_poison_fp8_cases(fa_poison, w):
+    """The fp8 parity cases (ragged, causal, GQA, one key, one query) with
+    their per-element E4M3 bound, on the poison build."""
+    fp8_tests.test_fp8_full_oracle(w)
 
 
 @pytest.mark.parametrize("name", ["pages_shape_h8_q4096_kv8192", "batched_prefill_b4h16_n2048_causal"])
