@@ -68,6 +68,12 @@ def lib():
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m exact_io_aware_17_amd.build`")
+        # torch ships its own HIP runtime under the same soname
+        # (libamdhip64.so.7). Loaded first, it satisfies the library's
+        # dependency; loaded after the library, it would be a second runtime
+        # in the process, and kernels launched through the system one on
+        # memory that torch's allocated fail to launch.
+        import torch  # noqa: F401
         handle = ctypes.CDLL(LIB_PATH)
         for name, (res, args) in SIGNATURES.items():
             fn = getattr(handle, name)

@@ -316,3 +316,26 @@ def test_binding_refuses_host_tensors_before_any_launch():
         fa._same_device(q, workspace=torch.empty(256, dtype=torch.uint8))
     with pytest.raises(ValueError, match="GPU"):
         fa.fa_combine(torch.empty(1, 2, 3, 16, 128), torch.empty(1, 2, 3, 16), o_cpu, lse_cpu)
+
+
+def test_library_shares_torchs_hip_runtime():
+    """Loading the library before torch has been imported must still leave a
+    single HIP runtime in the process (torch's): with two, kernels launched
+    through one on memory allocated by the other fail to launch. Run in a
+    fresh interpreter so that nothing has imported torch yet."""
+    import subprocess
+    import sys
+    code = (
+        "import os, sys\n"
+        f"sys.path.insert(0, {os.path.dirname(os.path.dirname(os.path.abspath(fa.__file__)))!r})\n"
+        "import exact_io_aware_17_amd as fa\n"
+        "fa.VERIFY_BUILD = False\n"
+        "fa.lib()\n"
+        "import torch\n"
+        "maps = {l.split()[-1] for l in open(f'/proc/{os.getpid()}/maps') if 'libamdhip64' in l}\n"
+        "print(len(maps), sorted(maps))\n"
+    )
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0, r.stderr[-2000:]
+    n = int(r.stdout.split()[0])
+    assert n == 1, f"HIP runtimes mapped: {r.stdout.strip()}"
