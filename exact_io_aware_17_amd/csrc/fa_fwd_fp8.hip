@@ -238,11 +238,20 @@ __global__ __launch_bounds__(kF8Threads) void fwd_fp8_kernel(
       // per score.
       const int L = causal && qrow + diag < Nk - 1 ? qrow + diag : Nk - 1;
       const int t = L - kv0 - 4 * hl;
+      // Each 32-key block is classified for the whole wave first (keys
+      // 32 mb + 0..27 in this lane's registers), as in the bf16 kernel.
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+      for (int mb = 0; mb < 2; ++mb) {
+        if (__all(mb * 32 + 27 <= t)) continue;
+        if (__all(mb * 32 > t)) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) sc[mb][i] = kNegInf;
+          continue;
+        }
 #pragma unroll
         for (int i = 0; i < 16; ++i)
           if (mb * 32 + (i >> 2) * 8 + (i & 3) > t) sc[mb][i] = kNegInf;
+      }
     }
     auto exps = [&]() __attribute__((always_inline)) {
       const float neg_m = -m_run;
