@@ -24,7 +24,9 @@
  *
  * Conventions shared by every entry point.
  *   - All tensor pointers are device pointers owned by the caller.  The
- *     library allocates nothing, frees nothing and keeps no global state.
+ *     library allocates nothing and frees nothing.  Its only global state is
+ *     the fixed scratch array of fa_fwd_splitkv_noalloc (below) and that
+ *     array's per-device address, looked up once.
  *   - bf16 tensors are IEEE bfloat16 bit patterns (uint16); fp32 are float.
  *   - Tensor pointers must be 16-byte aligned.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
