@@ -85,6 +85,35 @@ def test_bf16_row_groups_full_oracle(w):
     assert_close(errors(o, o_ref, lse, lse_ref), what=w.name)
 
 
+def _random_row_group_shapes(n=12, seed=2031):
+    """Seeded shapes whose grids take the row-group layouts: batch 1-2, 16,
+    32 or 64 KV heads with GQA 1/2/4, 1..519 rows and keys, d 64 or 128,
+    causal or not, kept only if there are at least 256 blocks of 256 rows
+    (or causal pairs of them)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        d = int(rng.choice([64, 128]))
+        hkv = int(rng.choice([16, 32, 64]))
+        hq = hkv * int(rng.choice([1, 2, 4]))
+        b, nq, nk, causal = int(rng.integers(1, 3)), int(rng.integers(1, 520)), int(rng.integers(1, 520)), bool(rng.integers(0, 2))
+        blocks = -(-nq // 256)
+        units = (blocks + 1) // 2 if causal and blocks >= 2 else blocks
+        if b * hq * units < 256:
+            continue
+        out.append(synth.Workload(f"rows_random_{len(out)}", b, hq, hkv, nq, nk, d, causal=causal, seed=400 + len(out)))
+    return out
+
+
+@pytest.mark.parametrize("w", _random_row_group_shapes(), ids=lambda w: w.name)
+def test_bf16_row_groups_random_shapes(w):
+    say(f"case bf16 row groups random {w.name}: B{w.B} Hq{w.Hq} Hkv{w.Hkv} {w.Nq}x{w.Nk} d{w.d} causal={w.causal}")
+    assert _fa().fa_fwd_layout(w.B, w.Hq, w.Nq, w.d, w.causal).startswith("rows")
+    o, lse = _run_fwd(w)
+    o_ref, lse_ref = oracle_full(w)
+    assert_close(errors(o, o_ref, lse, lse_ref), what=w.name)
+
+
 def _random_shapes(n=24, seed=2027):
     """Seeded mixed shapes: batch 1-2, 1-3 KV heads, GQA 1/2/4, 1..399 rows and
     keys, d 64, 128 or 256, with and without causal."""
