@@ -20,10 +20,10 @@
 //      are merged once at the end (same rescale, applied to the two halves).
 //      Twice the row blocks, for grids that 256-row blocks would leave short
 //      of the 256 CUs.
-//    Each tile copy costs its issuing wave time that the softmax is not
-//    running, and the copies per MFMA are what the two layouts differ in: row
-//    groups copy one K and one V tile per step for 512 MFMAs per SIMD pair,
-//    KV-parity groups two of each.
+//    Each tile copy instruction costs the step a fixed amount (whatever it
+//    moves, wherever it is issued), and the copies per MFMA are what the two
+//    layouts differ in: row groups copy one K and one V tile per step for 512
+//    MFMAs per SIMD pair, KV-parity groups two of each.
 //  * Scores are computed transposed, S^T = K Q^T, with 32x32x16 bf16 MFMAs.
 //    The wave's Q rows are the B operand and stay in registers for the whole
 //    loop; every lane then holds the scores of ONE query row, so the row max
@@ -430,8 +430,9 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_bf16_kernel(
   //   step s   phase A                           | phase B
   //   group 0: P.V 2s-2, scores 2s                 | copy K 2s+3, V 2s+1; softmax 2s
   //   group 1: copy K 2s+2, V 2s; softmax 2s-1     | P.V 2s-1, scores 2s+1
-  // Each group issues its copies at the start of its VALU phase (a copy costs
-  // the issuing wave some 50 cycles whatever it overlaps) and waits for them
+  // Each group issues its copies at the start of its VALU phase (as a burst:
+  // spreading them through the softmax or moving some into the MFMA phase
+  // gains nothing) and waits for them
   // one phase before the other group reads them: group 1 at the end of the
   // step, group 0 before the next mid-step barrier. Scores and probabilities
   // stay in registers across the barriers. Tile t lives in K slot t % 4 and V
